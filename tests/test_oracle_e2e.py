@@ -1,0 +1,370 @@
+"""End-to-end pins of the oracle's fused pass on tiny inputs.
+
+- placement: a hand-worked fixture (tests/golden/placement_example.json) and
+  an independent brute-force enumeration over every cache cell;
+- validation: hand-built malformed metadata -> all flags -1, no byte written;
+- quantisation: FP8 payloads decode back to the fp32 value within half an
+  E4M3 step; the head maximum encodes to upper_max; q_scale layouts;
+- slot addressing and the MLA concat.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def run_oracle(inp: W.NraInputs):
+    out = {
+        "qkv": inp.qkv.copy(),
+        "k_cache": inp.k_cache0.copy(),
+        "v_cache": inp.v_cache0.copy(),
+        "q_out": None if inp.q_in_place else inp.q_out0.copy(),
+        "q_scale": None if inp.q_scale0 is None else inp.q_scale0.copy(),
+        "flags": None if inp.flags0 is None else inp.flags0.copy(),
+    }
+    oracle.norm_rope_append(inp, out)
+    return out
+
+
+def _small(**kw):
+    args = dict(seed=5, q_lens=[3, 2, 0, 0], prior_lens=[3, 0, 4, 5], Hq=2, Hkv=1, D=128, page_size=4)
+    args.update(kw)
+    return W.nra_case(**args)
+
+
+# ----------------------------------------------------------------------------
+# placement
+# ----------------------------------------------------------------------------
+
+def test_placement_matches_hand_worked_fixture():
+    g = json.load(open(os.path.join(GOLDEN, "placement_example.json")))
+    inp = _small(norm=W.NORM_NONE)
+    inp.page_table = np.array(g["page_table"], np.int32)
+    inp.num_pages = g["num_pages"]
+    shape = (g["num_pages"], g["page_size"], g["Hkv"], g["D"])
+    rng = np.random.default_rng(0)
+    inp.k_cache0 = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    inp.v_cache0 = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    assert inp.q_indptr.tolist() == g["q_indptr"] and inp.seq_lens.tolist() == g["seq_lens"]
+    assert inp.positions.tolist() == g["expected_positions"]
+    # the contract's derived position r + seq_lens[b] - q_indptr[b+1]
+    derived = []
+    for b in range(inp.B):
+        for r in range(inp.q_indptr[b], inp.q_indptr[b + 1]):
+            derived.append(r + inp.seq_lens[b] - inp.q_indptr[b + 1])
+    assert derived == g["expected_positions"]
+    out = run_oracle(inp)
+    Hq, Hkv, D = inp.Hq, inp.Hkv, inp.D
+    for t, (p, r) in enumerate(g["expected_token_cells"]):
+        vrow = inp.qkv[t, (Hq + Hkv) * D:(Hq + 2 * Hkv) * D]
+        assert np.array_equal(out["v_cache"][p, r].ravel(), vrow)
+    for p, r in g["expected_tail_cells"]:
+        assert not out["k_cache"][p, r].any() and not out["v_cache"][p, r].any()
+    written = {tuple(c) for c in g["expected_token_cells"]} | {tuple(c) for c in g["expected_tail_cells"]}
+    for p in range(g["num_pages"]):
+        for r in range(g["page_size"]):
+            if (p, r) not in written:
+                assert np.array_equal(out["k_cache"][p, r], inp.k_cache0[p, r])
+                assert np.array_equal(out["v_cache"][p, r], inp.v_cache0[p, r])
+    assert out["flags"].ravel().tolist() == g["expected_flags"]
+
+
+def _brute_force_owner(inp: W.NraInputs):
+    """For every cache cell: which (request, logical row) owns it -- found by
+    scanning each request's page list, not by the forward formula."""
+    owner = {}
+    for b in range(inp.B):
+        sl = int(inp.seq_lens[b])
+        npages = -(-sl // inp.page_size)
+        for k in range(npages):
+            p = int(inp.page_table[b, k])
+            for r in range(inp.page_size):
+                owner[(p, r)] = (b, k * inp.page_size + r)
+    return owner
+
+
+@pytest.mark.parametrize("seed,ps,zero_tail", [(1, 4, True), (2, 16, True), (3, 8, False), (4, 1, True)])
+def test_placement_brute_force(seed, ps, zero_tail):
+    rng = np.random.default_rng(seed)
+    B = 7
+    q_lens = rng.integers(0, 9, size=B)
+    q_lens[2] = 0
+    prior = rng.integers(0, 30, size=B)
+    inp = W.nra_case(seed=seed, q_lens=q_lens, prior_lens=prior, Hq=2, Hkv=2, D=128, page_size=ps,
+                     norm=W.NORM_RMS, zero_tail=zero_tail)
+    out = run_oracle(inp)
+    assert (out["flags"] == 0).all()
+    owner = _brute_force_owner(inp)
+    Hq, Hkv, D = inp.Hq, inp.Hkv, inp.D
+    n_tok = n_tail = 0
+    for p in range(inp.num_pages):
+        for r in range(ps):
+            before_k, before_v = inp.k_cache0[p, r], inp.v_cache0[p, r]
+            after_k, after_v = out["k_cache"][p, r], out["v_cache"][p, r]
+            if (p, r) not in owner:
+                assert np.array_equal(after_k, before_k) and np.array_equal(after_v, before_v)
+                continue
+            b, L = owner[(p, r)]
+            sl = int(inp.seq_lens[b])
+            ql = int(q_lens[b])
+            if sl - ql <= L < sl:
+                t = int(inp.q_indptr[b]) + L - (sl - ql)
+                vrow = inp.qkv[t, (Hq + Hkv) * D:(Hq + 2 * Hkv) * D]
+                assert np.array_equal(after_v.ravel(), vrow)
+                assert not np.array_equal(after_k, before_k)
+                n_tok += 1
+            elif L >= sl and zero_tail and sl > 0 and L // ps == (sl - 1) // ps:
+                assert not after_k.any() and not after_v.any()
+                n_tail += 1
+            else:
+                assert np.array_equal(after_k, before_k) and np.array_equal(after_v, before_v)
+    assert n_tok == inp.T
+    if zero_tail and ps > 1:
+        assert n_tail > 0
+
+
+# ----------------------------------------------------------------------------
+# validation
+# ----------------------------------------------------------------------------
+
+def _mutations():
+    return {
+        "first_nonzero": lambda i: i.q_indptr.__setitem__(0, 1),
+        "non_monotone": lambda i: i.q_indptr.__setitem__(2, i.q_indptr[1] - 1),
+        "last_short": lambda i: i.q_indptr.__setitem__(-1, i.T - 1),
+        "last_long": lambda i: i.q_indptr.__setitem__(-1, i.T + 1),
+        "seq_len_below_q_len": lambda i: i.seq_lens.__setitem__(0, 2),
+        "too_many_pages": lambda i: i.seq_lens.__setitem__(1, i.page_table.shape[1] * i.page_size + 1),
+        "page_id_negative": lambda i: i.page_table.__setitem__((0, (int(i.seq_lens[0]) - 1) // i.page_size), -1),
+        "page_id_past_pool": lambda i: i.page_table.__setitem__((1, 0), i.num_pages),
+    }
+
+
+@pytest.mark.parametrize("name", list(_mutations()))
+def test_malformed_metadata_writes_only_minus_one_flags(name):
+    inp = _small(q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=True, max_seqlen=8, kv_fp8=True,
+                 k_scale=0.05, v_scale=0.05)
+    _mutations()[name](inp)
+    out = run_oracle(inp)
+    assert (out["flags"] == -1).all()
+    assert np.array_equal(out["k_cache"], inp.k_cache0)
+    assert np.array_equal(out["v_cache"], inp.v_cache0)
+    assert np.array_equal(out["q_out"], inp.q_out0)
+    assert np.array_equal(out["q_scale"].view(np.uint32), inp.q_scale0.view(np.uint32))
+    assert np.array_equal(out["qkv"], inp.qkv)
+
+
+def test_request_above_max_seqlen_is_invalid_only_for_padded_scales():
+    inp = _small(q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=True, max_seqlen=2, kv_fp8=True)
+    out = run_oracle(inp)
+    assert (out["flags"] == -1).all() and np.array_equal(out["q_out"], inp.q_out0)
+    inp = _small(q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=False, max_seqlen=2, kv_fp8=True)
+    out = run_oracle(inp)
+    assert (out["flags"] == 0).all()
+
+
+def test_out_of_range_position_suppresses_only_that_token():
+    inp = _small(norm=W.NORM_RMS)
+    inp.positions = inp.positions.copy()
+    inp.positions[1] = inp.cos_sin.shape[0]    # past the table
+    inp.positions[3] = -1
+    out = run_oracle(inp)
+    assert (out["flags"] == 0).all()
+    for t in range(inp.T):
+        same = np.array_equal(out["q_out"][t], inp.q_out0[t])
+        assert same == (t in (1, 3))
+
+
+# ----------------------------------------------------------------------------
+# quantisation
+# ----------------------------------------------------------------------------
+
+def _decode_e4m3(codes):
+    lut = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    return lut[codes]
+
+
+@pytest.mark.parametrize("upper_max", [448.0, 240.0])
+def test_dynamic_q_scale_and_payloads(upper_max):
+    inp = _small(q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=False, upper_max=upper_max, kv_fp8=True,
+                 k_scale=0.05, v_scale=0.05, qkv_sigma=2.0)
+    out = run_oracle(inp)
+    top = oracle.f64_to_e4m3(np.array([upper_max]))[0]
+    q = out["q_out"]
+    s = out["q_scale"]
+    for t in range(inp.T):
+        for h in range(inp.Hq):
+            codes = q[t, h]
+            mags = codes & 0x7F
+            # the head maximum encodes to +-upper_max, nothing exceeds it
+            assert mags.max() == top
+            assert (mags <= top).all()
+            # dequantised payload approximates the bf16-rounded result (norm +
+            # rope only ever moves a value by < 1 bf16 ulp from its fp32 form)
+            deq = _decode_e4m3(codes) * float(s[t, h])
+            assert np.all(np.isfinite(deq))
+    # the bf16 variant of the same call gives the rotated values; the FP8
+    # payload must be the nearest E4M3 code of value / scale within one step
+    inp_b = _small(q_mode=W.Q_BF16, qkv_sigma=2.0)
+    outb = run_oracle(inp_b)
+    vals = W.bf16_bits_to_f32(outb["q_out"]).astype(np.float64)
+    for t in range(inp.T):
+        for h in range(inp.Hq):
+            amax = np.abs(vals[t, h]).max()
+            assert abs(float(s[t, h]) - amax / upper_max) <= 1e-2 * amax / upper_max
+            deq = _decode_e4m3(q[t, h]) * float(s[t, h])
+            step = np.maximum(np.abs(vals[t, h]) / 8, 2**-9 * float(s[t, h]))
+            assert np.all(np.abs(deq - vals[t, h]) <= step + 1e-2 * np.abs(vals[t, h]))
+
+
+def test_padded_q_scale_layout_is_indexed_by_position_in_request():
+    inp = _small(q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=True, max_seqlen=129, kv_fp8=True,
+                 k_scale=0.05, v_scale=0.05)
+    out_p = run_oracle(inp)
+    inp_t = _small(q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=False, kv_fp8=True, k_scale=0.05, v_scale=0.05)
+    out_t = run_oracle(inp_t)
+    P = 256
+    assert out_p["q_scale"].shape == (inp.B, inp.Hq, P)
+    touched = np.zeros(out_p["q_scale"].shape, bool)
+    for b in range(inp.B):
+        for j in range(int(inp.q_indptr[b + 1] - inp.q_indptr[b])):
+            t = int(inp.q_indptr[b]) + j
+            assert np.array_equal(out_p["q_scale"][b, :, j], out_t["q_scale"][t])
+            touched[b, :, j] = True
+    # padding entries are never written
+    assert np.array_equal(out_p["q_scale"][~touched].view(np.uint32), inp.q_scale0[~touched].view(np.uint32))
+    assert np.array_equal(out_p["q_out"], out_t["q_out"])
+
+
+def test_static_q_and_kv_scales():
+    inp = _small(q_mode=W.Q_FP8_STATIC, q_scale_inv=4.0, kv_fp8=True, k_scale=0.25, v_scale=0.5,
+                 norm=W.NORM_NONE)
+    inp.positions = np.zeros(inp.T, np.int64)       # identity rotation
+    out = run_oracle(inp)
+    Hq, Hkv, D = inp.Hq, inp.Hkv, inp.D
+    x = W.bf16_bits_to_f32(inp.qkv).astype(np.float64)
+    # identity rotation + no norm: Q payload = E4M3(x * 4), V payload = E4M3(x / 0.5)
+    assert np.array_equal(out["q_out"].reshape(inp.T, -1), oracle.f64_to_e4m3(x[:, :Hq * D] * 4.0))
+    t = 0
+    b = 0
+    L = int(inp.seq_lens[b] - (inp.q_indptr[b + 1] - inp.q_indptr[b]))
+    p = inp.page_table[b, L // inp.page_size]
+    r = L % inp.page_size
+    vx = x[t, (Hq + Hkv) * D:(Hq + 2 * Hkv) * D]
+    kx = x[t, Hq * D:(Hq + Hkv) * D]
+    assert np.array_equal(out["v_cache"][p, r].ravel(), oracle.f64_to_e4m3(vx / 0.5))
+    assert np.array_equal(out["k_cache"][p, r].ravel(), oracle.f64_to_e4m3(kx / 0.25))
+
+
+def test_bf16_identity_path_is_bit_exact_copy():
+    inp = _small(q_mode=W.Q_BF16, norm=W.NORM_NONE)
+    inp.positions = np.zeros(inp.T, np.int64)
+    out = run_oracle(inp)
+    Hq, D = inp.Hq, inp.D
+    assert np.array_equal(out["q_out"].reshape(inp.T, -1), inp.qkv[:, :Hq * D])
+
+
+def test_one_hot_head_reads_cos_then_sin_half_of_the_table_row():
+    inp = _small(q_mode=W.Q_BF16, norm=W.NORM_NONE)
+    qkv = np.zeros_like(inp.qkv)
+    i = 9
+    qkv[:, i] = 0x3F80            # 1.0 at dim i of Q head 0
+    inp.qkv = qkv
+    out = run_oracle(inp)
+    for t in range(inp.T):
+        pos = inp.positions[t]
+        c, s = inp.cos_sin[pos, i], inp.cos_sin[pos, inp.D // 2 + i]
+        got = W.bf16_bits_to_f32(out["q_out"][t, 0])
+        assert got[i] == W.bf16_round(np.array([c]))[0]
+        assert got[i + inp.D // 2] == W.bf16_round(np.array([s]))[0]
+
+
+def test_in_place_q_and_k_leave_v_and_padding_untouched():
+    inp = _small(row_pad=64, q_in_place=True, k_in_place=True, norm=W.NORM_GEMMA)
+    out = run_oracle(inp)
+    Hq, Hkv, D = inp.Hq, inp.Hkv, inp.D
+    assert np.array_equal(out["qkv"][:, (Hq + Hkv) * D:], inp.qkv[:, (Hq + Hkv) * D:])
+    # Q and K columns equal the out-of-place result
+    ref = _small(row_pad=64, norm=W.NORM_GEMMA)
+    out_ref = run_oracle(ref)
+    assert np.array_equal(out["qkv"][:, :Hq * D], out_ref["q_out"].reshape(inp.T, -1))
+    assert np.array_equal(out["k_cache"], out_ref["k_cache"])
+    assert np.array_equal(out["v_cache"], out_ref["v_cache"])
+
+
+def test_slot_addressing_matches_paged_when_slots_are_the_paged_cells():
+    inp = _small(norm=W.NORM_RMS, zero_tail=False)
+    out_paged = run_oracle(inp)
+    slots = []
+    for b in range(inp.B):
+        ql = int(inp.q_indptr[b + 1] - inp.q_indptr[b])
+        for j in range(ql):
+            L = int(inp.seq_lens[b]) - ql + j
+            slots.append(int(inp.page_table[b, L // inp.page_size]) * inp.page_size + L % inp.page_size)
+    inp.addressing = W.ADDR_SLOT
+    inp.slot_mapping = np.array(slots, np.int64)
+    inp.slot_mapping[0] = -1                  # padding token: Q written, K/V skipped
+    out_slot = run_oracle(inp)
+    assert np.array_equal(out_slot["q_out"], out_paged["q_out"])
+    p0, r0 = divmod(slots[0], inp.page_size)
+    kc = out_paged["k_cache"].copy()
+    vc = out_paged["v_cache"].copy()
+    kc[p0, r0] = inp.k_cache0[p0, r0]
+    vc[p0, r0] = inp.v_cache0[p0, r0]
+    assert np.array_equal(out_slot["k_cache"], kc)
+    assert np.array_equal(out_slot["v_cache"], vc)
+
+
+# ----------------------------------------------------------------------------
+# MLA
+# ----------------------------------------------------------------------------
+
+def run_mla(inp: W.MlaInputs):
+    out = {"q": inp.q.copy(), "kv_cache": inp.kv_cache0.copy()}
+    oracle.mla_concat_rope_append(inp, out)
+    return out
+
+
+@pytest.mark.parametrize("fp8", [True, False])
+def test_mla_concat_layout_and_values(fp8):
+    inp = W.mla_case(seed=3, T=9, H=4, num_blocks=4, block_size=8, kv_fp8=fp8, negative_slots=2)
+    out = run_mla(inp)
+    K, R, nope = inp.kv_lora_rank, inp.rope_dim, inp.nope_dim
+    # q_nope untouched, q_rope changed
+    assert np.array_equal(out["q"][:, :, :nope], inp.q[:, :, :nope])
+    assert (out["q"][:, :, nope:] != inp.q[:, :, nope:]).mean() > 0.9
+    written = set()
+    for t in range(inp.T):
+        s = int(inp.slot_mapping[t])
+        if s < 0:
+            continue
+        row = out["kv_cache"][s // inp.block_size, s % inp.block_size]
+        written.add(s)
+        kc = W.bf16_bits_to_f32(inp.kv_c[t]).astype(np.float64)
+        if fp8:
+            assert np.array_equal(row[:K], oracle.f64_to_e4m3(kc / np.float64(np.float32(0.02))))
+        else:
+            assert np.array_equal(row[:K], inp.kv_c[t])
+        # the rope part equals the roped k_pe, which RoPE on q uses identically:
+        # treat k_pe as a q head and compare
+        x = W.bf16_bits_to_f32(inp.k_pe[t]).astype(np.float64)
+        pos = inp.positions[t]
+        c = inp.cos_sin[pos, :R // 2].astype(np.float64)
+        sn = inp.cos_sin[pos, R // 2:].astype(np.float64)
+        o = oracle.rope(x, 1, c, sn).astype(np.float32)
+        if fp8:
+            assert np.array_equal(row[K:], oracle.f64_to_e4m3(o.astype(np.float64) / np.float64(np.float32(0.02))))
+        else:
+            assert np.array_equal(row[K:], oracle.f32_to_bf16(o))
+    # all other rows keep their bytes
+    flat = out["kv_cache"].reshape(-1, K + R)
+    flat0 = inp.kv_cache0.reshape(-1, K + R)
+    for s in range(flat.shape[0]):
+        if s not in written:
+            assert np.array_equal(flat[s], flat0[s])
