@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Throughput of the fused prepare pass on one MI355X.
+
+One step = one pass of the whole norm-rope-append path over one batch of
+each workload the headline metric names:
+  * decode, B = 256 requests x 1 token, Hq/Hkv/D 32/8/128, bf16 Q and bf16
+    paged cache (page 16) over the full ~262k-page pool, tails cleared;
+  * ragged FP8 prefill, 8 requests (~15k tokens), 64/8/128, dynamic
+    per-token-head Q scales, E4M3 cache (page 64), tails cleared.
+Inputs are seeded and synthetic and already resident in HBM when the timed
+region starts.  `value` is the step's algorithmic bytes (qkv read + norm
+weights + cos/sin rows + Q write incl. q_scale + cache write incl. tail
+zeros) divided by the measured step time, in GB/s (1e9 B/s).
+
+Also reported: tokens/s, the roofline of the dominant kernel (the prefill
+launch, timed one launch at a time with HIP events on its stream after an
+L2/MALL flush), and the CPU oracle timed on the host on the same step.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of MI355X peak) + tokens/s, decode B=256 and prefill 16k tok"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--roofline-launches", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roofline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "mla"], default=None,
+                    help="time one workload alone (profiling runs)")
+    return ap.parse_args()
+
+
+class Call:
+    """Device-resident inputs and outputs of one norm-rope-append call."""
+
+    def __init__(self, inp, dev):
+        import numpy as np
+        import torch
+        import paged_kv_cache_token_amd as qp
+        import workloads as W
+        self.inp = inp
+
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(dt)
+
+        def seeded(nbytes, seed, dt, shape):
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed)
+            return torch.empty(nbytes, dtype=torch.uint8, device=dev).random_(0, 256, generator=g).view(dt).view(shape)
+
+        cdt = torch.uint8 if inp.kv_fp8 else torch.int16
+        cbytes = int(np.prod(inp.cache_shape)) * inp.kv_elt
+        self.qkv = up(inp.qkv, torch.int16)
+        self.k_cache = seeded(cbytes, inp.cache_seed, cdt, inp.cache_shape)
+        self.v_cache = seeded(cbytes, inp.cache_seed + 1, cdt, inp.cache_shape)
+        qdt = torch.int16 if inp.q_mode == W.Q_BF16 else torch.uint8
+        self.q_out = up(inp.q_out0, qdt)
+        self.q_scale = None if inp.q_scale0 is None else up(inp.q_scale0, torch.float32)
+        self.flags = up(inp.flags0, torch.int32)
+        sc = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)  # noqa: E731
+        self.kw = dict(
+            qkv=self.qkv, num_q_heads=inp.Hq, num_kv_heads=inp.Hkv, head_dim=inp.D, norm=inp.norm,
+            eps=inp.eps, q_norm_weight=up(inp.q_norm_weight, torch.float32),
+            k_norm_weight=up(inp.k_norm_weight, torch.float32), rope=inp.rope,
+            cos_sin_cache=up(inp.cos_sin, torch.float32), positions=up(inp.positions, torch.int64),
+            q_indptr=up(inp.q_indptr, torch.int32), seq_lens=up(inp.seq_lens, torch.int32),
+            page_table=up(inp.page_table, torch.int32), k_cache=self.k_cache, v_cache=self.v_cache,
+            kv_dtype=qp.FP8_E4M3 if inp.kv_fp8 else qp.BF16, k_scale=sc(inp.k_scale), v_scale=sc(inp.v_scale),
+            zero_tail=1, q_out=self.q_out, q_out_row_stride=inp.Hq * inp.D, q_mode=inp.q_mode,
+            q_scale=self.q_scale,
+            q_scale_layout=qp.QSCALE_REQ_HEAD_PADDED if inp.q_scale_padded else qp.QSCALE_TOKEN_HEAD,
+            max_seqlen=inp.max_seqlen, upper_max=inp.upper_max, flags=self.flags)
+        self.params = qp.norm_rope_append_params(**self.kw)
+        self.bytes = inp.algorithmic_bytes()["total"]
+
+    def launch(self, stream=None):
+        import paged_kv_cache_token_amd as qp
+        st = qp.call_norm_rope_append(self.params, stream)
+        if st != 0:
+            raise qp.QkprepError(st)
+
+
+class MlaCall:
+    def __init__(self, inp, dev):
+        import numpy as np
+        import torch
+        import paged_kv_cache_token_amd as qp
+        self.inp = inp
+
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(dt)
+        self.q = up(inp.q, torch.int16)
+        self.cache = up(inp.kv_cache0, torch.uint8)
+        self.params = qp.mla_params(
+            q=self.q, kv_c=up(inp.kv_c, torch.int16), k_pe=up(inp.k_pe, torch.int16),
+            cos_sin_cache=up(inp.cos_sin, torch.float32), positions=up(inp.positions, torch.int64),
+            slot_mapping=up(inp.slot_mapping, torch.int64), kv_cache=self.cache, num_q_heads=inp.H,
+            kv_scale=torch.tensor([inp.kv_scale], dtype=torch.float32, device=dev))
+        self.bytes = inp.algorithmic_bytes()["total"]
+
+    def launch(self, stream=None):
+        import paged_kv_cache_token_amd as qp
+        st = qp.call_mla_concat_rope_append(self.params, stream)
+        if st != 0:
+            raise qp.QkprepError(st)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("nra_kernel.hip", "qkprep_device.h", "qkprep_internal.h", "qkprep_api.hip"):
+        with open(os.path.join(ROOT, "paged_kv_cache_token_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel_hash: str):
+    """HBM bytes per launch of the prefill kernel from the committed rocprofv3
+    counter summary, valid only for the kernel source it was taken on."""
+    path = os.path.join(ROOT, "profiles", "nra_prefill_fp8_c3_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(c2, c3):
+    """The oracle (single-threaded C, fp64) on the same step: the decode call
+    on its touched pages and the full prefill call."""
+    import numpy as np
+    import oracle
+    t_total = 0.0
+    nbytes = 0
+    ntok = 0
+    for call in (c2, c3):
+        inp = call.inp
+        if inp.k_cache0 is None:
+            # decode pool is 17 GB: run the oracle on the touched pages only
+            import copy
+            import torch
+            pages = inp.touched_pages()
+            pidx = torch.from_numpy(pages).to(call.k_cache.device)
+            k0 = call.k_cache[pidx].cpu().numpy().view(np.uint16)
+            v0 = call.v_cache[pidx].cpu().numpy().view(np.uint16)
+            c = copy.copy(inp)
+            remap = np.full(inp.num_pages, -1, np.int64)
+            remap[pages] = np.arange(len(pages))
+            pt = inp.page_table.astype(np.int64)
+            c.page_table = np.where(pt >= 0, remap[np.clip(pt, 0, None)], -1).astype(np.int32)
+            c.num_pages = len(pages)
+            c.k_cache0, c.v_cache0 = k0, v0
+            inp = c
+        out = {"qkv": inp.qkv.copy(), "k_cache": inp.k_cache0.copy(), "v_cache": inp.v_cache0.copy(),
+               "q_out": inp.q_out0.copy(), "q_scale": None if inp.q_scale0 is None else inp.q_scale0.copy(),
+               "flags": inp.flags0.copy()}
+        t0 = time.perf_counter()
+        oracle.norm_rope_append(inp, out)
+        t_total += time.perf_counter() - t0
+        nbytes += call.bytes
+        ntok += inp.T
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(ntok / t_total, 1), "seconds": round(t_total, 3),
+            "sample": "one full step (decode B=256 on its touched pages + the ragged FP8 prefill call), "
+                      "single-threaded C oracle in fp64"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import paged_kv_cache_token_amd as qp  # noqa: F401  (fails loudly if libqkprep.so is missing)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log("generating decode B=256")
+    c2 = Call(W.c2_decode_b256(), dev)
+    log("generating ragged FP8 prefill")
+    c3 = Call(W.c3_prefill_fp8(), dev)
+    calls = {"decode": [c2], "prefill": [c3]}
+    if args.only == "mla":
+        calls = {"mla": [MlaCall(W.c5_mla(), dev)]}
+    elif args.only:
+        calls = {args.only: calls[args.only]}
+    step_calls = [c for v in calls.values() for c in v]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for c in step_calls:
+            c.launch()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for c in step_calls:
+            c.launch()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    step_bytes = sum(c.bytes for c in step_calls)
+    step_tokens = sum(c.inp.T for c in step_calls)
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    # per-launch times on the launch stream, each after a cache flush
+    breakdown = {}
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    dominant = None
+    if not args.no_roofline:
+        for name, cl in calls.items():
+            c = cl[0]
+            durs = []
+            for i in range(args.roofline_launches):
+                flush.fill_(i & 0xFF)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                c.launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                durs.append(e0.elapsed_time(e1) * 1e3)
+            durs.sort()
+            avg = sum(durs) / len(durs)
+            breakdown[name] = {"tokens": c.inp.T, "algorithmic_bytes": c.bytes, "avg_us": round(avg, 2),
+                               "median_us": round(durs[len(durs) // 2], 2),
+                               "GBps": round(c.bytes / (avg * 1e-6) / 1e9, 1),
+                               "Mtok_per_s": round(c.inp.T / avg, 2)}
+            if dominant is None or breakdown[name]["avg_us"] > breakdown[dominant]["avg_us"]:
+                dominant = name
+    del flush
+    log(f"step {ms:.4f} ms, {value:.1f} GB/s; {breakdown}")
+
+    roofline = None
+    if dominant is not None:
+        b = breakdown[dominant]
+        khash = kernel_source_hash()
+        traffic = recorded_traffic(khash) if dominant == "prefill" else None
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": b["GBps"], "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(b["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "algorithmic_bytes_per_launch": b["algorithmic_bytes"], "avg_launch_us": b["avg_us"],
+                    "kernel_source_hash": khash}
+
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        log("timing the CPU oracle on the same step")
+        cpu = cpu_baseline(c2, c3)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "tokens_per_s": round(step_tokens / (ms * 1e-3), 1),
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "config": {"workload": "decode B=256 (32/8/128 bf16, page 16, full pool) + ragged FP8 prefill "
+                               f"(8 req, T={c3.inp.T}, 64/8/128, page 64)",
+                   "step_tokens": step_tokens, "step_algorithmic_bytes": step_bytes,
+                   "calls": list(calls)},
+        "roofline": roofline, "cpu_baseline": cpu, "breakdown": breakdown,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

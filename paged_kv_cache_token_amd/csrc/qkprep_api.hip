@@ -1,0 +1,210 @@
+// C-ABI entry points of libqkprep: host-side argument checks, the empty-call
+// early return, launch-geometry choice and the single kernel launch.
+//
+// Host guards follow the review threads of the FlashInfer PR "fused QK
+// RMSNorm + NeoX RoPE + FP8 E4M3 quantize + NHD paged-KV append": an empty
+// batch returns without a launch, page_size <= 0 is rejected, invalid
+// upper_max / quant policy is rejected.  Nothing here reads device memory.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/qkprep.h"
+#include "qkprep_internal.h"
+
+using namespace qkprep;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int gcd_int(int a, int b) {
+    while (b) { int t = a % b; a = b; b = t; }
+    return a;
+}
+
+// tokens per tile: enough (token, chunk) items to give the 4 waves equal
+// runs; longer runs for large calls so a wave keeps one token's cos/sin for
+// all of that token's chunks
+int tokens_per_tile(int T, int cpt) {
+    int tpb = 4 / gcd_int(cpt, 4);
+    if (T >= 4096) {
+        while (tpb * cpt / 4 < cpt && tpb * 2 <= kMaxTokensPerTile) tpb *= 2;
+    }
+    return tpb;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qkprep_status_string(qkprep_status status) {
+    switch (status) {
+        case QKPREP_OK: return "ok";
+        case QKPREP_E_NULL: return "a required pointer is NULL";
+        case QKPREP_E_SHAPE: return "inconsistent sizes or strides";
+        case QKPREP_E_UNSUPPORTED: return "configuration not supported by this build";
+        case QKPREP_E_ALIGN: return "a vector-accessed base address or stride is not 16-byte aligned";
+        case QKPREP_E_RANGE: return "a scalar argument is outside its documented range";
+        case QKPREP_E_LAUNCH: return "the HIP kernel launch failed";
+        case QKPREP_E_VERSION: return "params.struct_size does not match this library";
+    }
+    return "unknown status";
+}
+
+int qkprep_abi_version(void) { return QKPREP_ABI_VERSION; }
+
+qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, hipStream_t stream) {
+    if (!p) return QKPREP_E_NULL;
+    if (p->struct_size != sizeof(qkprep_norm_rope_append_params)) return QKPREP_E_VERSION;
+    const int T = p->num_tokens, Hq = p->num_q_heads, Hkv = p->num_kv_heads, D = p->head_dim;
+    if (T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return QKPREP_E_SHAPE;
+    if (D != 128 && D != 256) return QKPREP_E_UNSUPPORTED;
+    if (p->rotary_dim != D) return QKPREP_E_UNSUPPORTED;
+    if (p->norm < 0 || p->norm > 2 || p->rope < 0 || p->rope > 1 || p->addressing < 0 ||
+        p->addressing > 1 || p->kv_dtype < 0 || p->kv_dtype > 1 || p->q_mode < 0 || p->q_mode > 2 ||
+        p->q_scale_layout < 0 || p->q_scale_layout > 1)
+        return QKPREP_E_RANGE;
+    if (p->page_size <= 0) return QKPREP_E_RANGE;
+    if (p->norm != 0 && !(p->eps > 0.0f && isfinite(p->eps))) return QKPREP_E_RANGE;
+    if (p->q_mode == QKPREP_Q_FP8_DYNAMIC && !(p->upper_max > 0.0f && p->upper_max <= 448.0f))
+        return QKPREP_E_RANGE;
+    const bool paged = p->addressing == QKPREP_ADDR_PAGED;
+    const int B = paged ? p->num_requests : 0;
+    const bool padded = p->q_mode == QKPREP_Q_FP8_DYNAMIC && p->q_scale_layout == QKPREP_QSCALE_REQ_HEAD_PADDED;
+    if (paged) {
+        if (B < 0) return QKPREP_E_SHAPE;
+        if (T > 0 && B == 0) return QKPREP_E_SHAPE;
+        if (B > kMaxRequests) return QKPREP_E_UNSUPPORTED;
+    } else if (padded) {
+        return QKPREP_E_UNSUPPORTED;   // the padded layout is indexed by request
+    }
+    if (padded && p->max_seqlen < 1) return QKPREP_E_RANGE;
+    // empty batch: nothing to write, no launch
+    if (T == 0 && B == 0) return QKPREP_OK;
+
+    const int R = Hq + 2 * Hkv;
+    const int kv_elt = p->kv_dtype == QKPREP_FP8_E4M3 ? 1 : 2;
+    const int q_elt = p->q_mode == QKPREP_Q_BF16 ? 2 : 1;
+    // pointers
+    if (!p->k_cache || !p->v_cache) return QKPREP_E_NULL;
+    if (p->kv_dtype == QKPREP_FP8_E4M3 && (!p->k_scale || !p->v_scale)) return QKPREP_E_NULL;
+    if (paged && (!p->q_indptr || !p->seq_lens || !p->page_table || !p->flags)) return QKPREP_E_NULL;
+    if (T > 0) {
+        if (!p->qkv || !p->cos_sin_cache || !p->positions || !p->q_out) return QKPREP_E_NULL;
+        if (p->norm != 0 && (!p->q_norm_weight || !p->k_norm_weight)) return QKPREP_E_NULL;
+        if (!paged && !p->slot_mapping) return QKPREP_E_NULL;
+        if (p->q_mode == QKPREP_Q_FP8_DYNAMIC && !p->q_scale) return QKPREP_E_NULL;
+        if (p->q_mode == QKPREP_Q_FP8_STATIC && !p->q_scale_inv) return QKPREP_E_NULL;
+    }
+    // sizes and strides
+    if (p->num_pages < 1) return QKPREP_E_SHAPE;
+    if (paged && p->max_pages_per_request < 1) return QKPREP_E_SHAPE;
+    const int64_t row_elems = (int64_t)Hkv * D;
+    if (p->k_page_stride < (int64_t)p->page_size * row_elems ||
+        p->v_page_stride < (int64_t)p->page_size * row_elems)
+        return QKPREP_E_SHAPE;
+    if ((p->k_page_stride * kv_elt) % 16 || (p->v_page_stride * kv_elt) % 16) return QKPREP_E_ALIGN;
+    if (!aligned16(p->k_cache) || !aligned16(p->v_cache)) return QKPREP_E_ALIGN;
+    if (T > 0) {
+        if (p->qkv_row_stride < (int64_t)R * D) return QKPREP_E_SHAPE;
+        if (p->qkv_row_stride % 8) return QKPREP_E_ALIGN;
+        if (p->q_out_row_stride < (int64_t)Hq * D) return QKPREP_E_SHAPE;
+        if ((p->q_out_row_stride * q_elt) % 16) return QKPREP_E_ALIGN;
+        if (p->cos_sin_rows < 1) return QKPREP_E_SHAPE;
+        if (!aligned16(p->qkv) || !aligned16(p->q_out) || !aligned16(p->cos_sin_cache)) return QKPREP_E_ALIGN;
+        if (p->norm != 0 && (!aligned16(p->q_norm_weight) || !aligned16(p->k_norm_weight)))
+            return QKPREP_E_ALIGN;
+        if (p->k_out) {
+            if (p->k_out_row_stride < row_elems) return QKPREP_E_SHAPE;
+            if (p->k_out_row_stride % 8 || !aligned16(p->k_out)) return QKPREP_E_ALIGN;
+        }
+    }
+
+    NraDevArgs a{};
+    a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.R = R;
+    a.qkv = static_cast<const uint16_t*>(p->qkv);
+    a.qkv_stride = p->qkv_row_stride;
+    a.norm = p->norm; a.eps = p->eps;
+    a.q_w = p->q_norm_weight; a.k_w = p->k_norm_weight;
+    a.rope = p->rope;
+    a.cos_sin = p->cos_sin_cache; a.cs_rows = p->cos_sin_rows;
+    a.positions = p->positions;
+    a.paged = paged ? 1 : 0;
+    a.B = B;
+    a.q_indptr = p->q_indptr; a.seq_lens = p->seq_lens; a.page_table = p->page_table;
+    a.maxp = p->max_pages_per_request;
+    a.slot_mapping = p->slot_mapping;
+    a.k_cache = p->k_cache; a.v_cache = p->v_cache;
+    a.num_pages = p->num_pages; a.page_size = p->page_size;
+    a.k_page_stride = p->k_page_stride; a.v_page_stride = p->v_page_stride;
+    a.k_scale = p->k_scale; a.v_scale = p->v_scale;
+    a.zero_tail = paged && p->zero_tail ? 1 : 0;
+    a.q_out = p->q_out; a.q_out_stride = p->q_out_row_stride;
+    a.q_scale = p->q_scale;
+    a.q_scale_padded = padded ? 1 : 0;
+    a.max_seqlen = p->max_seqlen;
+    a.q_scale_P = padded ? ((int64_t)p->max_seqlen + 127) / 128 * 128 : 0;
+    a.q_scale_inv = p->q_scale_inv;
+    a.upper_max = p->upper_max;
+    a.k_out = static_cast<uint16_t*>(p->k_out);
+    a.k_out_stride = p->k_out_row_stride;
+    a.flags = p->flags;
+    const int rows_per_wave = 64 / (D / 16);
+    a.chunks_per_token = (R + rows_per_wave - 1) / rows_per_wave;
+    a.tokens_per_tile = tokens_per_tile(T, a.chunks_per_token);
+    a.n_token_tiles = (T + a.tokens_per_tile - 1) / a.tokens_per_tile;
+    a.reqs_per_tile = B <= 2048 ? 1 : (B + 2047) / 2048;
+    a.n_req_tiles = B ? (B + a.reqs_per_tile - 1) / a.reqs_per_tile : 0;
+
+    hipError_t e = launch_norm_rope_append(a, D, p->q_mode, p->kv_dtype, stream);
+    return e == hipSuccess ? QKPREP_OK : QKPREP_E_LAUNCH;
+}
+
+qkprep_status qkprep_mla_concat_rope_append(const qkprep_mla_params* p, hipStream_t stream) {
+    if (!p) return QKPREP_E_NULL;
+    if (p->struct_size != sizeof(qkprep_mla_params)) return QKPREP_E_VERSION;
+    const int T = p->num_tokens;
+    if (T < 0 || p->num_q_heads < 1 || p->nope_dim < 0) return QKPREP_E_SHAPE;
+    if (p->rope_dim != 64) return QKPREP_E_UNSUPPORTED;
+    if (p->kv_lora_rank <= 0 || p->kv_lora_rank % 512) return QKPREP_E_UNSUPPORTED;
+    if (p->rope < 0 || p->rope > 1 || p->kv_dtype < 0 || p->kv_dtype > 1) return QKPREP_E_RANGE;
+    if (p->block_size <= 0) return QKPREP_E_RANGE;
+    if (T == 0) return QKPREP_OK;
+    if (!p->q || !p->kv_c || !p->k_pe || !p->cos_sin_cache || !p->positions || !p->slot_mapping ||
+        !p->kv_cache)
+        return QKPREP_E_NULL;
+    if (p->kv_dtype == QKPREP_FP8_E4M3 && !p->kv_scale) return QKPREP_E_NULL;
+    const int row_len = p->kv_lora_rank + p->rope_dim;
+    const int elt = p->kv_dtype == QKPREP_FP8_E4M3 ? 1 : 2;
+    if (p->num_blocks < 1 || p->cos_sin_rows < 1) return QKPREP_E_SHAPE;
+    if (p->q_head_stride < p->nope_dim + p->rope_dim) return QKPREP_E_SHAPE;
+    if (p->kv_c_stride < p->kv_lora_rank || p->k_pe_stride < p->rope_dim) return QKPREP_E_SHAPE;
+    if (p->block_stride < (int64_t)p->block_size * row_len) return QKPREP_E_SHAPE;
+    if (p->nope_dim % 8 || p->q_head_stride % 8 || p->q_token_stride % 8 || p->kv_c_stride % 8 ||
+        p->k_pe_stride % 8 || (p->block_stride * elt) % 16)
+        return QKPREP_E_ALIGN;
+    if (!aligned16(p->q) || !aligned16(p->kv_c) || !aligned16(p->k_pe) || !aligned16(p->cos_sin_cache) ||
+        !aligned16(p->kv_cache))
+        return QKPREP_E_ALIGN;
+
+    MlaDevArgs a{};
+    a.T = T; a.H = p->num_q_heads; a.nope_dim = p->nope_dim; a.kv_lora_rank = p->kv_lora_rank;
+    a.q = static_cast<uint16_t*>(p->q);
+    a.q_token_stride = p->q_token_stride; a.q_head_stride = p->q_head_stride;
+    a.kv_c = static_cast<const uint16_t*>(p->kv_c); a.kv_c_stride = p->kv_c_stride;
+    a.k_pe = static_cast<const uint16_t*>(p->k_pe); a.k_pe_stride = p->k_pe_stride;
+    a.rope = p->rope;
+    a.cos_sin = p->cos_sin_cache; a.cs_rows = p->cos_sin_rows;
+    a.positions = p->positions; a.slot_mapping = p->slot_mapping;
+    a.kv_cache = p->kv_cache;
+    a.capacity = p->num_blocks * (int64_t)p->block_size;
+    a.block_size = p->block_size; a.block_stride = p->block_stride;
+    a.kv_scale = p->kv_scale;
+    a.chunks_per_token = (a.H + 15) / 16 + 1;
+    a.tokens_per_tile = tokens_per_tile(T, a.chunks_per_token);
+    a.n_tiles = (T + a.tokens_per_tile - 1) / a.tokens_per_tile;
+    hipError_t e = launch_mla_concat_rope(a, p->kv_dtype, stream);
+    return e == hipSuccess ? QKPREP_OK : QKPREP_E_LAUNCH;
+}
+
+}  // extern "C"

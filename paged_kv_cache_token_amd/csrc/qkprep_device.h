@@ -1,0 +1,137 @@
+// Device-side building blocks of libqkprep for gfx950 (CDNA4, wave64).
+//
+// - 16-byte vector loads and stores of bf16 head rows;
+// - sums and maxima over the 8 or 16 lanes that hold one head row, built
+//   from DPP lane permutes that never leave that lane group (the sum of
+//   squares of an RMSNorm must cover one head of one token only: the review
+//   of TensorRT-LLM's fused preprocessing kernel found a warp-wide sum that
+//   mixed tokens);
+// - bf16 and OCP FP8 E4M3 packing with the gfx950 conversion instructions
+//   (v_cvt_pk_bf16_f32 rounds to nearest even; v_cvt_pk_fp8_f32 is used on
+//   inputs clamped to +-448 first, which makes it round-to-nearest-even with
+//   saturation, the "RN satfinite" of the FlashInfer contract).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkprep {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.0f;
+
+// ---------------------------------------------------------------------------
+// memory
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+    *reinterpret_cast<uint4*>(p) = v;
+}
+
+__device__ __forceinline__ void st8(void* p, uint2 v) {
+    *reinterpret_cast<uint2*>(p) = v;
+}
+
+__device__ __forceinline__ float4 ldf4(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// 8 bf16 values of a 16-byte vector -> fp32 x[0..7]
+__device__ __forceinline__ void unpack8(uint4 v, float* x) {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+// two fp32 -> two bf16 (round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2_t v = {a, b};
+    bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint4 pack8_bf16(const float* x) {
+    uint4 r;
+    r.x = pack_bf16x2(x[0], x[1]);
+    r.y = pack_bf16x2(x[2], x[3]);
+    r.z = pack_bf16x2(x[4], x[5]);
+    r.w = pack_bf16x2(x[6], x[7]);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// fp32 -> OCP E4M3, RN satfinite
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float sat448(float x) {
+    return __builtin_fminf(__builtin_fmaxf(x, -kE4M3Max), kE4M3Max);
+}
+
+// four fp32 -> four E4M3 bytes, x0 in the lowest byte
+__device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, float x3) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(x0), sat448(x1), 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(x2), sat448(x3), r, true);
+    return (uint32_t)r;
+}
+
+// eight fp32 (multiplied by `scale`) -> eight E4M3 bytes
+__device__ __forceinline__ uint2 pack8_fp8(const float* x, float scale) {
+    uint2 r;
+    r.x = pack_fp8x4(x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale);
+    r.y = pack_fp8x4(x[4] * scale, x[5] * scale, x[6] * scale, x[7] * scale);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// lane-group reductions (G = 8 or 16 lanes, aligned to multiples of G)
+// ---------------------------------------------------------------------------
+
+// DPP controls (gfx9 encoding)
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float,
+        __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the G consecutive lanes of a lane group; every lane of the
+// group receives the total.  All lanes of the group must be active.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(G == 8 || G == 16, "lane groups of 8 or 16");
+    v += dpp_f<kDppQuadSwap1>(v);
+    v += dpp_f<kDppQuadSwap2>(v);
+    v += dpp_f<kDppRowHalfMirror>(v);      // lane i <- lane 7 - i (other quad of the 8)
+    if constexpr (G == 16) v += dpp_f<kDppRowMirror>(v);  // lane i <- lane 15 - i
+    return v;
+}
+
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(G == 8 || G == 16, "lane groups of 8 or 16");
+    v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap1>(v));
+    v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap2>(v));
+    v = __builtin_fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+    if constexpr (G == 16) v = __builtin_fmaxf(v, dpp_f<kDppRowMirror>(v));
+    return v;
+}
+
+}  // namespace qkprep

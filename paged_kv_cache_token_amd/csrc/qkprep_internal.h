@@ -1,0 +1,92 @@
+// Launch descriptors shared by the C-ABI layer and the kernels of libqkprep.
+// Host-validated copies of the public params, flattened to what the device
+// needs, plus the launch geometry chosen on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qkprep {
+
+// Largest batch the norm-rope-append kernel stages in LDS (q_indptr,
+// seq_lens and a page-count prefix: 12 bytes per request).
+constexpr int kMaxRequests = 4096;
+constexpr int kBlockThreads = 256;
+constexpr int kMaxTokensPerTile = 16;
+
+struct NraDevArgs {
+    // shapes
+    int32_t T, Hq, Hkv, R;             // R = Hq + 2 Hkv head rows per token
+    const uint16_t* qkv;
+    int64_t qkv_stride;
+    int32_t norm;                       // 0 none, 1 rms, 2 gemma
+    float eps;
+    const float* q_w;
+    const float* k_w;
+    int32_t rope;                       // 0 neox, 1 interleaved
+    const float* cos_sin;
+    int64_t cs_rows;
+    const int64_t* positions;
+    int32_t paged;                      // 1 page table, 0 slot mapping
+    int32_t B;
+    const int32_t* q_indptr;
+    const int32_t* seq_lens;
+    const int32_t* page_table;
+    int32_t maxp;
+    const int64_t* slot_mapping;
+    void* k_cache;
+    void* v_cache;
+    int32_t num_pages, page_size;
+    int64_t k_page_stride, v_page_stride;
+    const float* k_scale;
+    const float* v_scale;
+    int32_t zero_tail;
+    void* q_out;
+    int64_t q_out_stride;
+    float* q_scale;
+    int32_t q_scale_padded;
+    int32_t max_seqlen;
+    int64_t q_scale_P;                  // padded row length round_up(max_seqlen, 128)
+    const float* q_scale_inv;
+    float upper_max;
+    uint16_t* k_out;
+    int64_t k_out_stride;
+    int32_t* flags;
+    // geometry
+    int32_t tokens_per_tile;            // TPB
+    int32_t chunks_per_token;           // CPT = ceil(R / rows per wave)
+    int32_t n_token_tiles;
+    int32_t n_req_tiles;
+    int32_t reqs_per_tile;
+};
+
+struct MlaDevArgs {
+    int32_t T, H, nope_dim, kv_lora_rank;
+    uint16_t* q;
+    int64_t q_token_stride, q_head_stride;
+    const uint16_t* kv_c;
+    int64_t kv_c_stride;
+    const uint16_t* k_pe;
+    int64_t k_pe_stride;
+    int32_t rope;
+    const float* cos_sin;
+    int64_t cs_rows;
+    const int64_t* positions;
+    const int64_t* slot_mapping;
+    void* kv_cache;
+    int64_t capacity;                   // num_blocks * block_size
+    int32_t block_size;
+    int64_t block_stride;
+    const float* kv_scale;
+    // geometry
+    int32_t tokens_per_tile;
+    int32_t chunks_per_token;           // ceil(H / heads per wave) + 1 latent chunk
+    int32_t n_tiles;
+};
+
+// returns hipSuccess or the launch error
+hipError_t launch_norm_rope_append(const NraDevArgs& a, int head_dim, int q_mode, int kv_fp8,
+                                   hipStream_t stream);
+hipError_t launch_mla_concat_rope(const MlaDevArgs& a, int kv_fp8, hipStream_t stream);
+
+}  // namespace qkprep

@@ -1,0 +1,309 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every case draws seeded inputs, runs libqkprep on the GPU and the oracle on
+host copies of the same inputs, and compares every output byte under the
+tolerances stated in tests/gpu_harness.py.  Guard bytes around every device
+buffer must survive each call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[case] {request.node.nodeid}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def run_and_compare(inp: W.NraInputs) -> dict:
+    dev = H.DeviceNra(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact(), "guard bytes around a device buffer changed"
+    gpu = dev.host_outputs()
+    ref = H.oracle_outputs(inp)
+    return H.compare_nra(inp, gpu, ref)
+
+
+# ----------------------------------------------------------------------------
+# the five configurations at full size
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c1", "c3", "c4"])
+def test_config_full_size(name):
+    inp = W.CONFIGS[name]()
+    stats = run_and_compare(inp)
+    print(name, inp.T, stats, flush=True)
+
+
+def test_c3_with_an_empty_request():
+    inp = W.c3_prefill_fp8(empty_request=3)
+    assert inp.q_indptr[4] == inp.q_indptr[3]
+    stats = run_and_compare(inp)
+    print(stats, flush=True)
+
+
+def test_c2_full_pool():
+    """B=256 decode over the full ~262k-page pool (17 GB of bf16 cache): the
+    touched pages are compared with the oracle run on a pool relabelled to
+    those pages; every other page must be byte-identical to its snapshot."""
+    inp = W.c2_decode_b256()
+    dev = H.DeviceNra(inp)
+    pages = inp.touched_pages()
+    pidx = torch.from_numpy(pages).to(H.DEV)
+    k_before = dev.k_cache.t[pidx].cpu().numpy().view(np.uint16)
+    v_before = dev.v_cache.t[pidx].cpu().numpy().view(np.uint16)
+    k_snap = dev.k_cache.t.clone()
+    v_snap = dev.v_cache.t.clone()
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    untouched = torch.ones(inp.num_pages, dtype=torch.bool, device=H.DEV)
+    untouched[pidx] = False
+    assert torch.equal(dev.k_cache.t[untouched], k_snap[untouched])
+    assert torch.equal(dev.v_cache.t[untouched], v_snap[untouched])
+    del k_snap, v_snap
+    gpu = dev.host_outputs(pages=pages)
+    cinp = H.compact_inputs(inp, k_before, v_before, pages)
+    ref = H.oracle_outputs(cinp)
+    stats = H.compare_nra(cinp, gpu, ref)
+    print(stats, flush=True)
+
+
+def test_c5_mla_full_size():
+    inp = W.c5_mla()
+    dev = H.DeviceMla(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    stats = H.compare_mla(inp, dev.host_outputs(), H.oracle_mla(inp))
+    print(stats, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# variants on small shapes (several tiles and a ragged tail)
+# ----------------------------------------------------------------------------
+
+def _ragged(seed, B=6, max_q=40, max_prior=300):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, max_q, size=B)
+    q[1] = 0
+    prior = rng.integers(0, max_prior, size=B)
+    return q, prior
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("norm", [W.NORM_NONE, W.NORM_RMS, W.NORM_GEMMA])
+@pytest.mark.parametrize("q_mode", [W.Q_BF16, W.Q_FP8_DYNAMIC, W.Q_FP8_STATIC])
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_variant_matrix(D, norm, q_mode, kv_fp8):
+    q, prior = _ragged(D + 10 * norm + 3 * q_mode + int(kv_fp8))
+    inp = W.nra_case(seed=int(q.sum()), q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=D, page_size=16,
+                     norm=norm, q_mode=q_mode, kv_fp8=kv_fp8, k_scale=0.07, v_scale=0.11,
+                     q_scale_inv=3.5, qkv_sigma=2.0)
+    run_and_compare(inp)
+
+
+@pytest.mark.parametrize("rope", [W.ROPE_NEOX, W.ROPE_INTERLEAVED])
+@pytest.mark.parametrize("heads", [(8, 1), (64, 8), (2, 2), (12, 4)])
+@pytest.mark.parametrize("ps", [1, 4, 64])
+def test_heads_pages_rope(rope, heads, ps):
+    q, prior = _ragged(heads[0] + ps + rope, B=5, max_q=20, max_prior=200)
+    inp = W.nra_case(seed=7 + ps, q_lens=q, prior_lens=prior, Hq=heads[0], Hkv=heads[1], D=128, page_size=ps,
+                     rope=rope, q_mode=W.Q_FP8_DYNAMIC, kv_fp8=True, k_scale=0.05, v_scale=0.05)
+    run_and_compare(inp)
+
+
+@pytest.mark.parametrize("qlen", [127, 128, 129])
+def test_dynamic_scale_padding_edge(qlen):
+    """4 requests x Q tokens with max_seqlen = Q: the padded q_scale row is
+    round_up(Q, 128) long and entries past Q are never written."""
+    inp = W.nra_case(seed=qlen, q_lens=[qlen] * 4, prior_lens=[0, 5, 64, 300], Hq=8, Hkv=1, D=128,
+                     page_size=16, norm=W.NORM_GEMMA, q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=True,
+                     max_seqlen=qlen, kv_fp8=True, k_scale=0.05, v_scale=0.05)
+    run_and_compare(inp)
+
+
+def test_upper_max_240():
+    q, prior = _ragged(240)
+    inp = W.nra_case(seed=240, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=16,
+                     q_mode=W.Q_FP8_DYNAMIC, upper_max=240.0, kv_fp8=True, k_scale=0.05, v_scale=0.05)
+    run_and_compare(inp)
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_strided_in_place(D):
+    q, prior = _ragged(D + 1)
+    inp = W.nra_case(seed=3, q_lens=q, prior_lens=prior, Hq=4, Hkv=2, D=D, page_size=8, row_pad=64,
+                     norm=W.NORM_GEMMA, q_in_place=True, k_in_place=True)
+    run_and_compare(inp)
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+def test_slot_addressing(kv_fp8):
+    q, prior = _ragged(17)
+    inp = W.nra_case(seed=17, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=16,
+                     addressing=W.ADDR_SLOT, kv_fp8=kv_fp8, q_mode=W.Q_FP8_DYNAMIC, k_scale=0.05,
+                     v_scale=0.05)
+    inp.slot_mapping = inp.slot_mapping.copy()
+    inp.slot_mapping[[0, 5]] = -1                                   # padding tokens
+    inp.slot_mapping[7] = inp.num_pages * inp.page_size + 3         # past the pool: skipped
+    run_and_compare(inp)
+
+
+def test_out_of_range_positions_suppress_tokens():
+    q, prior = _ragged(21)
+    inp = W.nra_case(seed=21, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=16)
+    inp.positions = inp.positions.copy()
+    inp.positions[[2, 9]] = [-5, inp.cos_sin.shape[0]]
+    run_and_compare(inp)
+
+
+def test_only_empty_requests():
+    inp = W.nra_case(seed=4, q_lens=[0, 0, 0], prior_lens=[5, 0, 33], Hq=8, Hkv=2, D=128, page_size=16)
+    assert inp.T == 0
+    run_and_compare(inp)
+
+
+def test_empty_call_launches_nothing():
+    inp = W.nra_case(seed=4, q_lens=[], prior_lens=[], Hq=8, Hkv=2, D=128, page_size=16)
+    dev = H.DeviceNra(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+
+
+@pytest.mark.parametrize("mutation", ["first_nonzero", "non_monotone", "last_short", "seq_len_below_q_len",
+                                      "too_many_pages", "page_id_negative", "page_id_past_pool",
+                                      "above_max_seqlen"])
+def test_malformed_metadata(mutation):
+    q, prior = _ragged(31)
+    q[0] = 5
+    inp = W.nra_case(seed=31, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=16,
+                     q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=True, max_seqlen=64, kv_fp8=True,
+                     k_scale=0.05, v_scale=0.05)
+    if mutation == "first_nonzero":
+        inp.q_indptr[0] = 1
+    elif mutation == "non_monotone":
+        inp.q_indptr[2] = inp.q_indptr[1] - 1
+    elif mutation == "last_short":
+        inp.q_indptr[-1] = inp.T - 1
+    elif mutation == "seq_len_below_q_len":
+        inp.seq_lens[0] = 2
+    elif mutation == "too_many_pages":
+        inp.seq_lens[3] = inp.page_table.shape[1] * inp.page_size + 1
+    elif mutation == "page_id_negative":
+        inp.page_table[0, (int(inp.seq_lens[0]) - 1) // inp.page_size] = -1
+    elif mutation == "page_id_past_pool":
+        inp.page_table[2, (int(inp.seq_lens[2]) - 1) // inp.page_size] = inp.num_pages
+    elif mutation == "above_max_seqlen":
+        inp.max_seqlen = 4
+    dev = H.DeviceNra(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    gpu = dev.host_outputs()
+    assert (gpu["flags"] == -1).all()
+    H.check_exact(gpu["k_cache"], inp.k_cache0, "k_cache")
+    H.check_exact(gpu["v_cache"], inp.v_cache0, "v_cache")
+    H.check_exact(gpu["q_out"], inp.q_out0, "q_out")
+    H.check_exact(gpu["q_scale"], inp.q_scale0, "q_scale")
+    H.check_exact(gpu["qkv"], inp.qkv, "qkv")
+    ref = H.oracle_outputs(inp)
+    assert (ref["flags"] == -1).all()
+
+
+def test_many_requests_cross_page_ragged():
+    rng = np.random.default_rng(99)
+    B = 300
+    q = rng.integers(0, 6, size=B)
+    prior = rng.integers(0, 100, size=B)
+    inp = W.nra_case(seed=99, q_lens=q, prior_lens=prior, Hq=16, Hkv=4, D=128, page_size=4,
+                     kv_fp8=True, k_scale=0.05, v_scale=0.05, q_mode=W.Q_FP8_STATIC, q_scale_inv=2.0)
+    run_and_compare(inp)
+
+
+# ----------------------------------------------------------------------------
+# MLA variants
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fp8", [True, False])
+@pytest.mark.parametrize("rope", [W.ROPE_INTERLEAVED, W.ROPE_NEOX])
+@pytest.mark.parametrize("H_", [128, 16, 20])
+def test_mla_variants(fp8, rope, H_):
+    inp = W.mla_case(seed=H_ + rope, T=77, H=H_, num_blocks=8, block_size=16, kv_fp8=fp8, rope=rope,
+                     negative_slots=3)
+    inp.positions = inp.positions.copy()
+    inp.positions[5] = -1
+    dev = H.DeviceMla(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    H.compare_mla(inp, dev.host_outputs(), H.oracle_mla(inp))
+
+
+# ----------------------------------------------------------------------------
+# determinism, idempotency, graph capture
+# ----------------------------------------------------------------------------
+
+def _snapshot(dev: H.DeviceNra):
+    return [b.raw.clone() for b in (dev.qkv, dev.k_cache, dev.v_cache, dev.q_out, dev.q_scale, dev.flags)
+            if b is not None]
+
+
+def _restore(dev: H.DeviceNra, snap):
+    for b, s in zip([b for b in (dev.qkv, dev.k_cache, dev.v_cache, dev.q_out, dev.q_scale, dev.flags)
+                     if b is not None], snap):
+        b.raw.copy_(s)
+
+
+def test_deterministic_and_idempotent():
+    q, prior = _ragged(55)
+    inp = W.nra_case(seed=55, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=16,
+                     q_mode=W.Q_FP8_DYNAMIC, kv_fp8=True, k_scale=0.05, v_scale=0.05)
+    dev = H.DeviceNra(inp)
+    before = _snapshot(dev)
+    dev.run()
+    first = _snapshot(dev)
+    dev.run()                       # a repeated call rewrites the same bytes
+    second = _snapshot(dev)
+    _restore(dev, before)
+    dev.run()
+    third = _snapshot(dev)
+    for a, b, c in zip(first, second, third):
+        assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_graph_capture_replays_match_eager():
+    q, prior = _ragged(77)
+    inp = W.nra_case(seed=77, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=16,
+                     q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=True, max_seqlen=64, kv_fp8=True,
+                     k_scale=0.05, v_scale=0.05)
+    dev = H.DeviceNra(inp)
+    before = _snapshot(dev)
+    dev.run()
+    torch.cuda.synchronize()
+    eager = _snapshot(dev)
+    _restore(dev, before)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            dev.run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _restore(dev, before)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = _snapshot(dev)
+        for a, b in zip(eager, got):
+            assert torch.equal(a, b), f"replay {rep} differs from eager"
