@@ -75,7 +75,11 @@ class Call:
         self.k_cache = seeded(cbytes, inp.cache_seed, cdt, inp.cache_shape)
         self.v_cache = seeded(cbytes, inp.cache_seed + 1, cdt, inp.cache_shape)
         qdt = torch.int16 if inp.q_mode == W.Q_BF16 else torch.uint8
-        self.q_out = up(inp.q_out0, qdt)
+        self.q_out = self.qkv if inp.q_in_place else up(inp.q_out0, qdt)
+        k_out = None
+        if inp.k_in_place:
+            k_out = self.qkv.view(-1)[inp.Hq * inp.D:].as_strided((inp.T, inp.Hkv * inp.D),
+                                                                  (inp.qkv_row_stride, 1))
         self.q_scale = None if inp.q_scale0 is None else up(inp.q_scale0, torch.float32)
         self.flags = up(inp.flags0, torch.int32)
         sc = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)  # noqa: E731
@@ -87,7 +91,9 @@ class Call:
             q_indptr=up(inp.q_indptr, torch.int32), seq_lens=up(inp.seq_lens, torch.int32),
             page_table=up(inp.page_table, torch.int32), k_cache=self.k_cache, v_cache=self.v_cache,
             kv_dtype=qp.FP8_E4M3 if inp.kv_fp8 else qp.BF16, k_scale=sc(inp.k_scale), v_scale=sc(inp.v_scale),
-            zero_tail=1, q_out=self.q_out, q_out_row_stride=inp.Hq * inp.D, q_mode=inp.q_mode,
+            zero_tail=1, q_out=self.q_out, q_out_row_stride=inp.qkv_row_stride if inp.q_in_place else inp.Hq * inp.D,
+            q_mode=inp.q_mode, k_out=k_out, k_out_row_stride=inp.qkv_row_stride, qkv_row_stride=inp.qkv_row_stride,
+            q_scale_inv=sc(inp.q_scale_inv), num_tokens=inp.T,
             q_scale=self.q_scale,
             q_scale_layout=qp.QSCALE_REQ_HEAD_PADDED if inp.q_scale_padded else qp.QSCALE_TOKEN_HEAD,
             max_seqlen=inp.max_seqlen, upper_max=inp.upper_max, flags=self.flags)

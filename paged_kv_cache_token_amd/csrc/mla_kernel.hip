@@ -151,8 +151,8 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
                 unpack8(ld16(kp + kHalf), x + 8);
                 rope16(x, c, s, a.rope);
                 if constexpr (KVFP8) {
-                    st8(dst + K + 8 * gl, pack8_fp8(x, inv_scale));
-                    st8(dst + K + kHalf + 8 * gl, pack8_fp8(x + 8, inv_scale));
+                    store_fp8_row(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf, pack8_fp8(x, inv_scale),
+                                  pack8_fp8(x + 8, inv_scale));
                 } else {
                     st16(dst + K + 8 * gl, pack8_bf16(x));
                     st16(dst + K + kHalf + 8 * gl, pack8_bf16(x + 8));

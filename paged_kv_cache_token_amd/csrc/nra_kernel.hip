@@ -78,20 +78,15 @@ __device__ __forceinline__ ReqPages request_pages(const NraDevArgs& a, const int
     return r;
 }
 
-// Block-wide verdict over the whole call (see file comment).  Fills
-// s_indptr[0..B], s_seqlen[0..B) and s_pre[0..B] (exclusive prefix of the
-// per-request page counts).  Returns non-zero when the call is invalid.
-__device__ int validate_call(const NraDevArgs& a, int* s_indptr, int* s_seqlen, int* s_pre,
-                             int* s_wave) {
+// Validation, step 1 (LDS only): per-request checks and the block-wide
+// exclusive prefix s_pre[0..B] of the number of pages each request writes.
+// Needs s_indptr / s_seqlen staged.  Returns this thread's partial verdict.
+__device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen, int* s_pre,
+                                 int* s_wave) {
     const int tid = threadIdx.x;
     const int B = a.B;
     int bad = 0;
-    for (int i = tid; i <= B; i += kBlockThreads) s_indptr[i] = a.q_indptr[i];
-    for (int i = tid; i < B; i += kBlockThreads) s_seqlen[i] = a.seq_lens[i];
-    __syncthreads();
     if (tid == 0 && (s_indptr[0] != 0 || s_indptr[B] != a.T)) bad = 1;
-
-    // per-thread run of consecutive requests -> page counts -> block scan
     const int per = (B + kBlockThreads - 1) / kBlockThreads;
     const int lo = min(B, tid * per), hi = min(B, lo + per);
     int sum = 0;
@@ -118,282 +113,424 @@ __device__ int validate_call(const NraDevArgs& a, int* s_indptr, int* s_seqlen, 
     }
     if (tid == kBlockThreads - 1) s_pre[B] = base + incl;
     __syncthreads();
-
-    // every page id the call writes must lie in the pool
-    const int total = s_pre[B];
-    for (int k = tid; k < total; k += kBlockThreads) {
-        const int b = lds_upper_bound(s_pre, B + 1, k) - 1;
-        const ReqPages rp = request_pages(a, s_indptr, s_seqlen, b);
-        const int pidx = rp.first + (k - s_pre[b]);
-        const int p = a.page_table[(int64_t)b * a.maxp + pidx];
-        if (p < 0 || p >= a.num_pages) bad = 1;
-    }
-    return __syncthreads_or(bad);
+    return bad;
 }
+
+// Validation, step 2: every page id the call writes must lie in the pool.
+// Thread k checks pages k, k + 256, ...; page_id_at() issues one load.
+__device__ __forceinline__ int page_id_at(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen,
+                                          const int* s_pre, int k) {
+    const int b = lds_upper_bound(s_pre, a.B + 1, k) - 1;
+    const ReqPages rp = request_pages(a, s_indptr, s_seqlen, b);
+    return a.page_table[(int64_t)b * a.maxp + rp.first + (k - s_pre[b])];
+}
+
+__device__ __forceinline__ int page_out_of_pool(const NraDevArgs& a, int p) {
+    return (p < 0 || p >= a.num_pages) ? 1 : 0;
+}
+
+template <int D, int QMODE, bool KVFP8>
+struct KvType {
+    typedef typename std::conditional<KVFP8, uint8_t, uint16_t>::type type;
+};
+
+// Encodes and stores head row r of tile token ti (global token t) whose two
+// 16-byte vectors v0 / v1 are in registers.  Q/K rows: RMSNorm (weights
+// from LDS), RoPE (cos/sin row from LDS), then bf16 / E4M3.  V rows: copy
+// or E4M3.  `c` holds the per-call constants.
+struct RowConsts {
+    float inv_k, inv_v, q_static, inv_um;
+    int qs_hstride;
+};
+
+template <int D, int QMODE, bool KVFP8>
+__device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, int r, int gl, uint4 v0, uint4 v1,
+                                            const float* s_w, const float* s_cs_row, const int64_t* s_koff,
+                                            const int64_t* s_voff, const int64_t* s_qsoff, const RowConsts& k) {
+    constexpr int G = D / 16;
+    constexpr int HALF = D / 2;
+    typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
+    if (r >= a.Hq + a.Hkv) {
+        // V head: raw copy (bf16 cache) or x / v_scale (FP8 cache)
+        const int64_t voff = s_voff[ti];
+        if (voff < 0) return;
+        kv_t* dst = reinterpret_cast<kv_t*>(a.v_cache) + voff + (r - a.Hq - a.Hkv) * D + 8 * gl;
+        if constexpr (KVFP8) {
+            float x[16];
+            unpack8(v0, x);
+            unpack8(v1, x + 8);
+            store_fp8_row(reinterpret_cast<uint8_t*>(dst) - 8 * gl, gl, HALF, pack8_fp8(x, k.inv_v),
+                          pack8_fp8(x + 8, k.inv_v));
+        } else {
+            st16(dst, v0);
+            st16(dst + HALF, v1);
+        }
+        return;
+    }
+    const bool is_q = r < a.Hq;
+    float x[16];
+    unpack8(v0, x);
+    unpack8(v1, x + 8);
+    if (a.norm != 0) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss = fmaf(x[i], x[i], ss);
+        ss = group_sum<G>(ss);
+        const float inv = rsqrtf(fmaf(ss, 1.0f / (float)D, a.eps));
+        const float* w = s_w + (is_q ? 0 : D);
+        const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * gl);
+        const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * gl + 4);
+        const float4 w2 = *reinterpret_cast<const float4*>(w + HALF + 8 * gl);
+        const float4 w3 = *reinterpret_cast<const float4*>(w + HALF + 8 * gl + 4);
+        const float wv[16] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w,
+                              w2.x, w2.y, w2.z, w2.w, w3.x, w3.y, w3.z, w3.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = x[i] * inv * wv[i];
+    }
+    if (a.rope == 0) {
+        // NeoX: pair i of the lane = dims (8 gl + i, D/2 + 8 gl + i), angle 8 gl + i
+        const float4 c0 = *reinterpret_cast<const float4*>(s_cs_row + 8 * gl);
+        const float4 c1 = *reinterpret_cast<const float4*>(s_cs_row + 8 * gl + 4);
+        const float4 s0 = *reinterpret_cast<const float4*>(s_cs_row + HALF + 8 * gl);
+        const float4 s1 = *reinterpret_cast<const float4*>(s_cs_row + HALF + 8 * gl + 4);
+        const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float xa = x[i], xb = x[8 + i];
+            x[i] = xa * c[i] - xb * s[i];
+            x[8 + i] = xb * c[i] + xa * s[i];
+        }
+    } else {
+        // interleaved: the first vector holds angles 4 gl .. 4 gl + 3, the
+        // second D/4 + 4 gl .. D/4 + 4 gl + 3
+        const float4 c0 = *reinterpret_cast<const float4*>(s_cs_row + 4 * gl);
+        const float4 c1 = *reinterpret_cast<const float4*>(s_cs_row + D / 4 + 4 * gl);
+        const float4 s0 = *reinterpret_cast<const float4*>(s_cs_row + HALF + 4 * gl);
+        const float4 s1 = *reinterpret_cast<const float4*>(s_cs_row + HALF + D / 4 + 4 * gl);
+        const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int i0 = (m < 4) ? 2 * m : 8 + 2 * (m - 4);
+            const float xa = x[i0], xb = x[i0 + 1];
+            x[i0] = xa * c[m] - xb * s[m];
+            x[i0 + 1] = xb * c[m] + xa * s[m];
+        }
+    }
+    if (is_q) {
+        const int h = r;
+        if constexpr (QMODE == 0) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(a.q_out) + (int64_t)t * a.q_out_stride + h * D + 8 * gl;
+            st16(dst, pack8_bf16(x));
+            st16(dst + HALF, pack8_bf16(x + 8));
+        } else {
+            uint8_t* dst = reinterpret_cast<uint8_t*>(a.q_out) + (int64_t)t * a.q_out_stride + h * D + 8 * gl;
+            float mul = k.q_static;
+            if constexpr (QMODE == 1) {
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+                amax = group_max<G>(amax);
+                // s = max(amax, 1e-6) / upper_max; payload = x * (1 / s)
+                const float sc = __builtin_fmaxf(amax, 1e-6f) * k.inv_um;
+                mul = __builtin_amdgcn_rcpf(sc);
+                if (gl == 0) a.q_scale[s_qsoff[ti] + (int64_t)h * k.qs_hstride] = sc;
+            }
+            store_fp8_row(dst - 8 * gl, gl, HALF, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
+        }
+    } else {
+        const int kh = r - a.Hq;
+        const int64_t koff = s_koff[ti];
+        if (koff >= 0) {
+            kv_t* dst = reinterpret_cast<kv_t*>(a.k_cache) + koff + kh * D + 8 * gl;
+            if constexpr (KVFP8) {
+                store_fp8_row(reinterpret_cast<uint8_t*>(dst) - 8 * gl, gl, HALF, pack8_fp8(x, k.inv_k),
+                              pack8_fp8(x + 8, k.inv_k));
+            } else {
+                st16(dst, pack8_bf16(x));
+                st16(dst + HALF, pack8_bf16(x + 8));
+            }
+        }
+        if (a.k_out) {
+            uint16_t* ko = a.k_out + (int64_t)t * a.k_out_stride + kh * D + 8 * gl;
+            st16(ko, pack8_bf16(x));
+            st16(ko + HALF, pack8_bf16(x + 8));
+        }
+    }
+}
+
+// (token, chunk) cursor over a wave's run of items; chunk c of token t
+// covers head rows [c * RPW, c * RPW + RPW).
+struct Cursor {
+    int t, c, left;
+    __device__ __forceinline__ void advance(int cpt) {
+        const bool wrap = c + 1 == cpt;
+        c = wrap ? 0 : c + 1;
+        t += wrap ? 1 : 0;
+        --left;
+    }
+};
 
 template <int D, int QMODE, bool KVFP8>
 __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) {
     constexpr int G = D / 16;        // lanes per head row
     constexpr int RPW = 64 / G;      // head rows per wave
     constexpr int HALF = D / 2;
+    constexpr int U = kBatch;
+    constexpr int D4 = D / 4;        // float4 per cos/sin row
+    typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
 
     extern __shared__ int s_dyn[];   // q_indptr [B+1] | seq_lens [B] | page prefix [B+1]
     __shared__ int s_wave[4];
+    __shared__ __align__(16) float s_w[2 * D];                       // q | k norm weights
+    __shared__ __align__(16) float s_cs[kMaxTokensPerTile * D];      // cos/sin rows of the tile
     __shared__ int s_pos[kMaxTokensPerTile];
     __shared__ int64_t s_koff[kMaxTokensPerTile];
     __shared__ int64_t s_voff[kMaxTokensPerTile];
     __shared__ int64_t s_qsoff[kMaxTokensPerTile];
+    __shared__ int s_tail[kTailPrefetch];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int grp = lane / G;        // head-row slot of this lane in the wave
     const int gl = lane % G;         // lane inside the head row
-
     int* s_indptr = s_dyn;
     int* s_seqlen = s_dyn + (a.B + 1);
     int* s_pre = s_dyn + (2 * a.B + 1);
 
-    int bad = 0;
-    if (a.paged) bad = validate_call(a, s_indptr, s_seqlen, s_pre, s_wave);
-
-    // per-lane norm weights for the lane's 16 dims
-    float wq[16], wk[16];
-    if (a.norm != 0) {
-        const float add = (a.norm == 2) ? 1.0f : 0.0f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int off = h * HALF + 8 * gl;
-            float4 q0 = ldf4(a.q_w + off), q1 = ldf4(a.q_w + off + 4);
-            float4 k0 = ldf4(a.k_w + off), k1 = ldf4(a.k_w + off + 4);
-            wq[8 * h + 0] = q0.x + add; wq[8 * h + 1] = q0.y + add;
-            wq[8 * h + 2] = q0.z + add; wq[8 * h + 3] = q0.w + add;
-            wq[8 * h + 4] = q1.x + add; wq[8 * h + 5] = q1.y + add;
-            wq[8 * h + 6] = q1.z + add; wq[8 * h + 7] = q1.w + add;
-            wk[8 * h + 0] = k0.x + add; wk[8 * h + 1] = k0.y + add;
-            wk[8 * h + 2] = k0.z + add; wk[8 * h + 3] = k0.w + add;
-            wk[8 * h + 4] = k1.x + add; wk[8 * h + 5] = k1.y + add;
-            wk[8 * h + 6] = k1.z + add; wk[8 * h + 7] = k1.w + add;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { wq[i] = 1.0f; wk[i] = 1.0f; }
-    }
-    const float inv_k = KVFP8 ? 1.0f / *a.k_scale : 1.0f;
-    const float inv_v = KVFP8 ? 1.0f / *a.v_scale : 1.0f;
-    const float q_static = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
-    const float inv_D = 1.0f / (float)D;
-
-    typedef typename std::conditional<KVFP8, uint8_t, uint16_t>::type kv_t;
-    kv_t* kc = reinterpret_cast<kv_t*>(a.k_cache);
-    kv_t* vc = reinterpret_cast<kv_t*>(a.v_cache);
-    const int64_t row_elems = (int64_t)a.Hkv * D;
-    const int TPB = a.tokens_per_tile;
     const int CPT = a.chunks_per_token;
-    const int n_tiles = a.n_req_tiles + a.n_token_tiles;
+    const int TPB = a.tokens_per_tile;
+    const int64_t row_elems = (int64_t)a.Hkv * D;
+    const int blo = (int)((int64_t)a.total_items * blockIdx.x / gridDim.x);
+    const int bhi = (int)((int64_t)a.total_items * (blockIdx.x + 1) / gridDim.x);
 
-    for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-        if (tile < a.n_req_tiles) {
-            // ---------------- request tile: flags and tail clear ----------------
-            for (int bi = 0; bi < a.reqs_per_tile; ++bi) {
-                const int b = tile * a.reqs_per_tile + bi;
-                if (b >= a.B) break;
-                for (int h = tid; h < a.Hkv; h += kBlockThreads)
-                    a.flags[(int64_t)b * a.Hkv + h] = bad ? -1 : 0;
-                if (bad || !a.zero_tail) continue;
-                const int sl = s_seqlen[b];
-                if (sl <= 0) continue;
-                const int last = (sl - 1) % a.page_size;
-                const int64_t page = a.page_table[(int64_t)b * a.maxp + (sl - 1) / a.page_size];
-                const int64_t nvec = (int64_t)(a.page_size - 1 - last) * row_elems * sizeof(kv_t) / 16;
-                char* kb = reinterpret_cast<char*>(kc + page * a.k_page_stride + (last + 1) * row_elems);
-                char* vb = reinterpret_cast<char*>(vc + page * a.v_page_stride + (last + 1) * row_elems);
-                const uint4 z = make_uint4(0, 0, 0, 0);
-                for (int64_t i = tid; i < nvec; i += kBlockThreads) {
-                    st16(kb + 16 * i, z);
-                    st16(vb + 16 * i, z);
-                }
-            }
-            continue;
+    uint4 bufA[U][2], bufB[U][2];
+    Cursor ld{0, 0, 0}, pr{0, 0, 0};
+    int sub_lo = blo, t_first = 0, ntok = 0, sub_hi = blo;
+    // Loads of the next U head rows of the wave's run (no metadata needed).
+    // Always exactly 2 U loads, with rows past the run or past R clamped to a
+    // valid row: the compiler's wait counters then stay exact, and a wait for
+    // one batch never has to drain the batch issued after it.
+    auto load_batch = [&](uint4 (&buf)[U][2]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int r = ld.c * RPW + grp;
+            const bool ok = ld.left > 0 && r < a.R;
+            const int rr = ok ? r : 0;
+            const int tt = ld.left > 0 ? ld.t : t_first;
+            const uint16_t* src = a.qkv + (int64_t)tt * a.qkv_stride + rr * D + 8 * gl;
+            buf[u][0] = ld16(src);
+            buf[u][1] = ld16(src + HALF);
+            ld.advance(CPT);
         }
-        if (bad) continue;
-
-        // ---------------- token tile ----------------
-        const int t0 = (tile - a.n_req_tiles) * TPB;
-        if (tid < TPB) {
-            const int t = t0 + tid;
-            int pos = -1;
-            int64_t koff = -1, voff = -1, qsoff = 0;
-            if (t < a.T) {
-                const int64_t p64 = a.positions[t];
-                if (p64 >= 0 && p64 < a.cs_rows) pos = (int)p64;
-                if (a.paged) {
-                    const int b = lds_upper_bound(s_indptr, a.B + 1, t) - 1;
-                    const int beg = s_indptr[b];
-                    const int ql = s_indptr[b + 1] - beg;
-                    const int j = t - beg;
-                    const int L = s_seqlen[b] - ql + j;
-                    const int64_t page = a.page_table[(int64_t)b * a.maxp + L / a.page_size];
-                    const int64_t row = L % a.page_size;
+    };
+    // tile bounds and this wave's run inside it
+    auto start_tile = [&]() {
+        t_first = sub_lo / CPT;
+        sub_hi = min(bhi, (t_first + TPB) * CPT);
+        ntok = (sub_hi - 1) / CPT - t_first + 1;
+        const int n = sub_hi - sub_lo;
+        const int w_lo = sub_lo + n * wave / 4;
+        const int w_hi = sub_lo + n * (wave + 1) / 4;
+        ld.t = w_lo / CPT;
+        ld.c = w_lo - ld.t * CPT;
+        ld.left = w_hi - w_lo;
+        pr = ld;
+    };
+    // per-token metadata that needs no request lookup (position, slot)
+    auto stage_positions = [&]() {
+        if (tid < ntok) {
+            const int t = t_first + tid;
+            const int64_t p64 = a.positions[t];
+            s_pos[tid] = (p64 >= 0 && p64 < a.cs_rows) ? (int)p64 : -1;
+            if (!a.paged) {
+                int64_t koff = -1, voff = -1;
+                const int64_t slot = a.slot_mapping[t];
+                if (slot >= 0 && slot < (int64_t)a.num_pages * a.page_size) {
+                    const int64_t page = slot / a.page_size, row = slot % a.page_size;
                     koff = page * a.k_page_stride + row * row_elems;
                     voff = page * a.v_page_stride + row * row_elems;
-                    qsoff = a.q_scale_padded ? (int64_t)b * a.Hq * a.q_scale_P + j : (int64_t)t * a.Hq;
-                } else {
-                    const int64_t slot = a.slot_mapping[t];
-                    if (slot >= 0 && slot < (int64_t)a.num_pages * a.page_size) {
-                        const int64_t page = slot / a.page_size, row = slot % a.page_size;
-                        koff = page * a.k_page_stride + row * row_elems;
-                        voff = page * a.v_page_stride + row * row_elems;
-                    }
-                    qsoff = (int64_t)t * a.Hq;
                 }
+                s_koff[tid] = koff;
+                s_voff[tid] = voff;
+                s_qsoff[tid] = (int64_t)t * a.Hq;
             }
-            s_pos[tid] = pos;
-            s_koff[tid] = koff;
-            s_voff[tid] = voff;
-            s_qsoff[tid] = qsoff;
         }
-        __syncthreads();
+    };
+    // request lookup, page and cos/sin row of every tile token (needs s_pos)
+    auto stage_rows = [&]() {
+        if (a.paged && tid < ntok) {
+            const int t = t_first + tid;
+            const int b = lds_upper_bound(s_indptr, a.B + 1, t) - 1;
+            const int beg = s_indptr[b];
+            const int ql = s_indptr[b + 1] - beg;
+            const int j = t - beg;
+            const int L = s_seqlen[b] - ql + j;
+            const int64_t page = a.page_table[(int64_t)b * a.maxp + L / a.page_size];
+            const int64_t row = L % a.page_size;
+            s_koff[tid] = page * a.k_page_stride + row * row_elems;
+            s_voff[tid] = page * a.v_page_stride + row * row_elems;
+            s_qsoff[tid] = a.q_scale_padded ? (int64_t)b * a.Hq * a.q_scale_P + j : (int64_t)t * a.Hq;
+        }
+        for (int k = tid; k < ntok * D4; k += kBlockThreads) {
+            const int i = k / D4;
+            const int c4 = k - i * D4;
+            const int p = s_pos[i];
+            if (p >= 0) *reinterpret_cast<float4*>(s_cs + i * D + 4 * c4) = ldf4(a.cos_sin + (int64_t)p * D + 4 * c4);
+        }
+    };
 
-        const int n_items = TPB * CPT;
-        const int ipw = (n_items + 3) >> 2;
-        const int it_lo = wave * ipw;
-        const int it_hi = min(n_items, it_lo + ipw);
-        const int qs_hstride = a.q_scale_padded ? (int)a.q_scale_P : 1;
-        int cur_ti = -1;
-        float c[8], s[8];
-        for (int it = it_lo; it < it_hi; ++it) {
-            const int ti = it / CPT;
-            const int chunk = it - ti * CPT;
-            const int t = t0 + ti;
-            if (t >= a.T) break;
-            const int pos = s_pos[ti];
-            if (pos < 0) continue;
-            if (ti != cur_ti) {
-                cur_ti = ti;
-                const float* cs = a.cos_sin + (int64_t)pos * D;
-                if (a.rope == 0) {
-                    // NeoX: pair k of the lane has angle 8*gl + k
-                    float4 c0 = ldf4(cs + 8 * gl), c1 = ldf4(cs + 8 * gl + 4);
-                    float4 s0 = ldf4(cs + HALF + 8 * gl), s1 = ldf4(cs + HALF + 8 * gl + 4);
-                    c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
-                    c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
-                    s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
-                    s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
-                } else {
-                    // interleaved: first vector holds angles 4*gl .. 4*gl+3,
-                    // second vector angles D/4 + 4*gl .. D/4 + 4*gl + 3
-                    float4 c0 = ldf4(cs + 4 * gl), c1 = ldf4(cs + D / 4 + 4 * gl);
-                    float4 s0 = ldf4(cs + HALF + 4 * gl), s1 = ldf4(cs + HALF + D / 4 + 4 * gl);
-                    c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
-                    c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
-                    s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
-                    s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
-                }
-            }
-            const int r = chunk * RPW + grp;          // head row of this lane group
-            if (r >= a.R) continue;                   // idle group (lane-group uniform)
-            const uint16_t* src = a.qkv + (int64_t)t * a.qkv_stride + (int64_t)r * D + 8 * gl;
-            const uint4 v0 = ld16(src);
-            const uint4 v1 = ld16(src + HALF);
-            if (r >= a.Hq + a.Hkv) {
-                // V head: raw copy (bf16 cache) or x / v_scale (FP8 cache)
-                const int64_t voff = s_voff[ti];
-                if (voff < 0) continue;
-                kv_t* dst = vc + voff + (int64_t)(r - a.Hq - a.Hkv) * D + 8 * gl;
-                if constexpr (KVFP8) {
-                    float x[16];
-                    unpack8(v0, x);
-                    unpack8(v1, x + 8);
-                    st8(dst, pack8_fp8(x, inv_v));
-                    st8(dst + HALF, pack8_fp8(x + 8, inv_v));
-                } else {
-                    st16(dst, v0);
-                    st16(dst + HALF, v1);
-                }
-                continue;
-            }
-            const bool is_q = r < a.Hq;
-            float x[16];
-            unpack8(v0, x);
-            unpack8(v1, x + 8);
-            if (a.norm != 0) {
-                float ss = 0.0f;
+    // page ids of the tails this workgroup clears (first kTailPrefetch requests)
+    const int r_lo = (int)((int64_t)a.B * blockIdx.x / gridDim.x);
+    const int r_hi = (int)((int64_t)a.B * (blockIdx.x + 1) / gridDim.x);
+    auto stage_tails = [&]() {
+        const int b = r_lo + tid;
+        if (tid < kTailPrefetch && b < r_hi) {
+            const int sl = s_seqlen[b];
+            s_tail[tid] = (a.zero_tail && sl > 0)
+                              ? a.page_table[(int64_t)b * a.maxp + (sl - 1) / a.page_size] : -1;
+        }
+    };
+
+    // ---- first tile: its qkv loads go out before the metadata chain ----
+    const bool have_items = blo < bhi;
+    if (have_items) {
+        start_tile();
+        load_batch(bufA);
+    }
+    if (a.norm != 0) {
+        const float add = (a.norm == 2) ? 1.0f : 0.0f;
+        for (int i = tid; i < 2 * D; i += kBlockThreads) s_w[i] = (i < D ? a.q_w[i] : a.k_w[i - D]) + add;
+    }
+    if (a.paged) {
+        for (int i = tid; i <= a.B; i += kBlockThreads) s_indptr[i] = a.q_indptr[i];
+        for (int i = tid; i < a.B; i += kBlockThreads) s_seqlen[i] = a.seq_lens[i];
+    }
+    if (have_items) stage_positions();
+    __syncthreads();
+    int bad = 0;
+    if (a.paged) bad = __syncthreads_or(validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave));
+    if (!bad) {
+        // With every request consistent, page-table reads stay inside each
+        // request's row.  The page-id checks, the tile's row lookups and cos/sin
+        // loads and the tail-page prefetch are independent: all issue at once.
+        int p_first = 0;
+        const int total_pages = a.paged ? s_pre[a.B] : 0;
+        if (tid < total_pages) p_first = page_id_at(a, s_indptr, s_seqlen, s_pre, tid);
+        if (have_items) stage_rows();
+        if (a.paged) stage_tails();
+        if (tid < total_pages) bad |= page_out_of_pool(a, p_first);
+        for (int k = tid + kBlockThreads; k < total_pages; k += kBlockThreads)
+            bad |= page_out_of_pool(a, page_id_at(a, s_indptr, s_seqlen, s_pre, k));
+    }
+    bad = __syncthreads_or(bad);
+
+    RowConsts kc;
+    kc.inv_k = KVFP8 ? 1.0f / *a.k_scale : 1.0f;
+    kc.inv_v = KVFP8 ? 1.0f / *a.v_scale : 1.0f;
+    kc.q_static = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
+    kc.inv_um = (QMODE == 1) ? 1.0f / a.upper_max : 1.0f;
+    kc.qs_hstride = a.q_scale_padded ? (int)a.q_scale_P : 1;
+
+    auto run_batch = [&](uint4 (&buf)[U][2]) {
 #pragma unroll
-                for (int k = 0; k < 16; ++k) ss = fmaf(x[k], x[k], ss);
-                ss = group_sum<G>(ss);
-                const float inv = rsqrtf(fmaf(ss, inv_D, a.eps));
-#pragma unroll
-                for (int k = 0; k < 16; ++k) x[k] = x[k] * inv * (is_q ? wq[k] : wk[k]);
-            }
-            if (a.rope == 0) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float xa = x[k], xb = x[8 + k];
-                    x[k] = xa * c[k] - xb * s[k];
-                    x[8 + k] = xb * c[k] + xa * s[k];
-                }
-            } else {
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int i0 = (m < 4) ? 2 * m : 8 + 2 * (m - 4);
-                    const float xa = x[i0], xb = x[i0 + 1];
-                    x[i0] = xa * c[m] - xb * s[m];
-                    x[i0 + 1] = xb * c[m] + xa * s[m];
-                }
-            }
-            if (is_q) {
-                const int h = r;
-                if constexpr (QMODE == 0) {
-                    uint16_t* dst = reinterpret_cast<uint16_t*>(a.q_out) + (int64_t)t * a.q_out_stride +
-                                    (int64_t)h * D + 8 * gl;
-                    st16(dst, pack8_bf16(x));
-                    st16(dst + HALF, pack8_bf16(x + 8));
-                } else {
-                    uint8_t* dst = reinterpret_cast<uint8_t*>(a.q_out) + (int64_t)t * a.q_out_stride +
-                                   (int64_t)h * D + 8 * gl;
-                    float mul = q_static;
-                    if constexpr (QMODE == 1) {
-                        float amax = 0.0f;
-#pragma unroll
-                        for (int k = 0; k < 16; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[k]));
-                        amax = group_max<G>(amax);
-                        const float sc = __builtin_fmaxf(amax, 1e-6f) / a.upper_max;
-                        mul = 1.0f / sc;
-                        if (gl == 0) a.q_scale[s_qsoff[ti] + (int64_t)h * qs_hstride] = sc;
-                    }
-                    st8(dst, pack8_fp8(x, mul));
-                    st8(dst + HALF, pack8_fp8(x + 8, mul));
-                }
-            } else {
-                const int kh = r - a.Hq;
-                const int64_t koff = s_koff[ti];
-                if (koff >= 0) {
-                    kv_t* dst = kc + koff + (int64_t)kh * D + 8 * gl;
-                    if constexpr (KVFP8) {
-                        st8(dst, pack8_fp8(x, inv_k));
-                        st8(dst + HALF, pack8_fp8(x + 8, inv_k));
-                    } else {
-                        st16(dst, pack8_bf16(x));
-                        st16(dst + HALF, pack8_bf16(x + 8));
-                    }
-                }
-                if (a.k_out) {
-                    uint16_t* ko = a.k_out + (int64_t)t * a.k_out_stride + (int64_t)kh * D + 8 * gl;
-                    st16(ko, pack8_bf16(x));
-                    st16(ko + HALF, pack8_bf16(x + 8));
-                }
+        for (int u = 0; u < U; ++u) {
+            if (pr.left > 0) {
+                const int r = pr.c * RPW + grp;
+                const int ti = pr.t - t_first;
+                if (r < a.R && s_pos[ti] >= 0)
+                    process_row<D, QMODE, KVFP8>(a, pr.t, ti, r, gl, buf[u][0], buf[u][1], s_w, s_cs + ti * D,
+                                                 s_koff, s_voff, s_qsoff, kc);
+                pr.advance(CPT);
             }
         }
-        __syncthreads();   // the next tile rewrites the per-token LDS arrays
+    };
+
+    // ------------------ requests: flags and tail clear ------------------
+    // (issued before the token items so the zero stores drain while the
+    // rows are processed)
+    for (int b = r_lo; a.paged && b < r_hi; ++b) {
+        for (int h = tid; h < a.Hkv; h += kBlockThreads) a.flags[(int64_t)b * a.Hkv + h] = bad ? -1 : 0;
+        if (bad || !a.zero_tail) continue;
+        const int sl = s_seqlen[b];
+        if (sl <= 0) continue;
+        const int last = (sl - 1) % a.page_size;
+        const int64_t page = (b - r_lo < kTailPrefetch)
+                                 ? (int64_t)s_tail[b - r_lo]
+                                 : (int64_t)a.page_table[(int64_t)b * a.maxp + (sl - 1) / a.page_size];
+        const int64_t nvec = (int64_t)(a.page_size - 1 - last) * row_elems * (int64_t)sizeof(kv_t) / 16;
+        char* kb = reinterpret_cast<char*>(reinterpret_cast<kv_t*>(a.k_cache) + page * a.k_page_stride +
+                                           (last + 1) * row_elems);
+        char* vb = reinterpret_cast<char*>(reinterpret_cast<kv_t*>(a.v_cache) + page * a.v_page_stride +
+                                           (last + 1) * row_elems);
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        for (int64_t i = tid; i < nvec; i += kBlockThreads) {
+            st16(kb + 16 * i, z);
+            st16(vb + 16 * i, z);
+        }
     }
+
+    // ---------------------------- token items ----------------------------
+    if (have_items && !bad) {
+        for (;;) {
+            // double-buffered: the next batch's loads are issued before the
+            // current batch's stores
+            while (pr.left > 0) {
+                load_batch(bufB);
+                run_batch(bufA);
+                if (pr.left <= 0) break;
+                load_batch(bufA);
+                run_batch(bufB);
+            }
+            sub_lo = sub_hi;
+            if (sub_lo >= bhi) break;
+            __syncthreads();   // every wave is done with this tile's LDS rows
+            start_tile();
+            load_batch(bufA);
+            stage_positions();
+            __syncthreads();
+            stage_rows();
+            __syncthreads();
+        }
+    }
+
+
+}
+
+// workgroups per CU the kernel can keep resident (queried once per device)
+template <int D, int QMODE, bool KVFP8>
+int resident_blocks(size_t lds) {
+    static int cached_dev = -1, cached = 0, cached_cus = 0;
+    static size_t cached_lds = (size_t)-1;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev != cached_dev || lds != cached_lds) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nra_kernel<D, QMODE, KVFP8>, kBlockThreads,
+                                                         lds) != hipSuccess)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+        cached = (per_cu < 1 ? 1 : per_cu) * cus;
+        cached_cus = cus;
+        cached_dev = dev;
+        cached_lds = lds;
+    }
+    (void)cached_cus;
+    return cached;
 }
 
 template <int D, int QMODE, bool KVFP8>
 hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
-    const int n_tiles = a.n_req_tiles + a.n_token_tiles;
-    const int grid = n_tiles < 8192 ? n_tiles : 8192;
     const size_t lds = a.paged ? (size_t)(3 * a.B + 2) * sizeof(int) : 0;
+    // enough workgroups to fill every CU, none with less than 8 head-row
+    // chunks of work, and at least one per 4 requests for the tail clears
+    const int64_t cap = resident_blocks<D, QMODE, KVFP8>(lds);
+    int64_t want = (a.total_items + 7) / 8;
+    if (want < (a.B + 3) / 4) want = (a.B + 3) / 4;
+    if (want < 1) want = 1;
+    const int grid = (int)(want < cap ? want : cap);
     hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8>), dim3(grid), dim3(kBlockThreads), lds, stream, a);
     return hipGetLastError();
 }

@@ -8,7 +8,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/qkprep.h"
+#include "qkprep.h"
 #include "qkprep_internal.h"
 
 using namespace qkprep;
@@ -151,10 +151,8 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     a.flags = p->flags;
     const int rows_per_wave = 64 / (D / 16);
     a.chunks_per_token = (R + rows_per_wave - 1) / rows_per_wave;
-    a.tokens_per_tile = tokens_per_tile(T, a.chunks_per_token);
-    a.n_token_tiles = (T + a.tokens_per_tile - 1) / a.tokens_per_tile;
-    a.reqs_per_tile = B <= 2048 ? 1 : (B + 2047) / 2048;
-    a.n_req_tiles = B ? (B + a.reqs_per_tile - 1) / a.reqs_per_tile : 0;
+    a.tokens_per_tile = kMaxTokensPerTile;
+    a.total_items = (int64_t)T * a.chunks_per_token;
 
     hipError_t e = launch_norm_rope_append(a, D, p->q_mode, p->kv_dtype, stream);
     return e == hipSuccess ? QKPREP_OK : QKPREP_E_LAUNCH;

@@ -134,4 +134,23 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// ---------------------------------------------------------------------------
+// one 16-byte store per lane for an FP8 head row
+// ---------------------------------------------------------------------------
+
+// Lane gl of a head-row group holds the E4M3 codes of dims [8 gl, 8 gl + 8)
+// (lo) and [half + 8 gl, half + 8 gl + 8) (hi).  Neighbouring lanes swap one
+// 8-byte half so that even lanes store dims [8 gl, 8 gl + 16) and odd lanes
+// dims [half + 8 gl - 8, half + 8 gl + 8): one 16-byte store per lane, and
+// the group writes whole 128-byte lines.
+__device__ __forceinline__ void store_fp8_row(uint8_t* row, int gl, int half, uint2 lo, uint2 hi) {
+    const bool odd = gl & 1;
+    const uint2 send = odd ? lo : hi;
+    uint2 recv;
+    recv.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.x, kDppQuadSwap1, 0xF, 0xF, false);
+    recv.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.y, kDppQuadSwap1, 0xF, 0xF, false);
+    const uint4 v = odd ? make_uint4(recv.x, recv.y, hi.x, hi.y) : make_uint4(lo.x, lo.y, recv.x, recv.y);
+    st16(row + (odd ? half + 8 * (gl - 1) : 8 * gl), v);
+}
+
 }  // namespace qkprep

@@ -13,6 +13,10 @@ namespace qkprep {
 constexpr int kMaxRequests = 4096;
 constexpr int kBlockThreads = 256;
 constexpr int kMaxTokensPerTile = 16;
+// head rows each wave has in flight per load batch (double-buffered)
+constexpr int kBatch = 2;
+// tail pages of the first requests a workgroup clears, prefetched with the metadata
+constexpr int kTailPrefetch = 16;
 
 struct NraDevArgs {
     // shapes
@@ -52,12 +56,11 @@ struct NraDevArgs {
     uint16_t* k_out;
     int64_t k_out_stride;
     int32_t* flags;
-    // geometry
-    int32_t tokens_per_tile;            // TPB
-    int32_t chunks_per_token;           // CPT = ceil(R / rows per wave)
-    int32_t n_token_tiles;
-    int32_t n_req_tiles;
-    int32_t reqs_per_tile;
+    // geometry: every workgroup owns a balanced, contiguous range of the
+    // T * chunks_per_token (token, chunk) items and of the B requests
+    int32_t tokens_per_tile;            // most tokens staged in LDS at once
+    int32_t chunks_per_token;           // ceil(R / head rows per wave)
+    int64_t total_items;                // T * chunks_per_token
 };
 
 struct MlaDevArgs {

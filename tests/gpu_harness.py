@@ -45,7 +45,7 @@ class Guarded:
             g = torch.Generator(device=DEV)
             g.manual_seed(fill_seed)
             body.random_(0, 256, generator=g)
-        self.t = body.view(dtype).view(shape) if nbytes else body.view(dtype)
+        self.t = body.view(dtype).view(shape)
 
     def guards_intact(self) -> bool:
         head = self.raw[:GUARD]
