@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     __shared__ int s_pos[kMaxTokensPerTile];
     __shared__ int64_t s_row[kMaxTokensPerTile];   // element offset of the cache row, -1 = skip
 
+    preload_kernargs(a);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -68,7 +69,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     typedef typename std::conditional<KVFP8, uint8_t, uint16_t>::type kv_t;
     kv_t* cache = reinterpret_cast<kv_t*>(a.kv_cache);
 
-    for (int tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    for (int tile = blockIdx.x; tile < a.n_tiles; tile += a.grid) {
         const int t0 = tile * TPB;
         if (tid < TPB) {
             const int t = t0 + tid;
@@ -165,8 +166,9 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
 
 template <bool KVFP8>
 hipError_t launch_t(const MlaDevArgs& a, hipStream_t stream) {
-    const int grid = a.n_tiles < 8192 ? a.n_tiles : 8192;
-    hipLaunchKernelGGL((mla_kernel<KVFP8>), dim3(grid), dim3(kBlockThreads), 0, stream, a);
+    MlaDevArgs la = a;
+    la.grid = a.n_tiles < 8192 ? a.n_tiles : 8192;
+    hipLaunchKernelGGL((mla_kernel<KVFP8>), dim3(la.grid), dim3(kBlockThreads), 0, stream, la);
     return hipGetLastError();
 }
 

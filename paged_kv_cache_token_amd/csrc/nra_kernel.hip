@@ -23,7 +23,7 @@
 //    split into 4 contiguous runs, one per wave, so a wave usually keeps one
 //    token's cos/sin for several chunks.  A request tile clears the tails of
 //    its requests' last pages and writes their flags.  The grid is
-//    persistent: workgroup w takes tiles w, w + gridDim.x, ...
+//    persistent: workgroup w takes tiles w, w + a.grid, ...
 //  * All-or-nothing validation without a host sync or a second kernel:
 //    every workgroup stages q_indptr / seq_lens in LDS, checks every request
 //    and every page id the call will write (the pages are enumerated
@@ -291,6 +291,7 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     __shared__ int64_t s_qsoff[kMaxTokensPerTile];
     __shared__ int s_tail[kTailPrefetch];
 
+    preload_kernargs(a);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -303,8 +304,8 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     const int CPT = a.chunks_per_token;
     const int TPB = a.tokens_per_tile;
     const int64_t row_elems = (int64_t)a.Hkv * D;
-    const int blo = (int)((int64_t)a.total_items * blockIdx.x / gridDim.x);
-    const int bhi = (int)((int64_t)a.total_items * (blockIdx.x + 1) / gridDim.x);
+    const int blo = (int)((int64_t)a.total_items * blockIdx.x / a.grid);
+    const int bhi = (int)((int64_t)a.total_items * (blockIdx.x + 1) / a.grid);
 
     uint4 bufA[U][2], bufB[U][2];
     Cursor ld{0, 0, 0}, pr{0, 0, 0};
@@ -383,8 +384,8 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     };
 
     // page ids of the tails this workgroup clears (first kTailPrefetch requests)
-    const int r_lo = (int)((int64_t)a.B * blockIdx.x / gridDim.x);
-    const int r_hi = (int)((int64_t)a.B * (blockIdx.x + 1) / gridDim.x);
+    const int r_lo = (int)((int64_t)a.B * blockIdx.x / a.grid);
+    const int r_hi = (int)((int64_t)a.B * (blockIdx.x + 1) / a.grid);
     auto stage_tails = [&]() {
         const int b = r_lo + tid;
         if (tid < kTailPrefetch && b < r_hi) {
@@ -530,8 +531,9 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     int64_t want = (a.total_items + 7) / 8;
     if (want < (a.B + 3) / 4) want = (a.B + 3) / 4;
     if (want < 1) want = 1;
-    const int grid = (int)(want < cap ? want : cap);
-    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8>), dim3(grid), dim3(kBlockThreads), lds, stream, a);
+    NraDevArgs la = a;
+    la.grid = (int)(want < cap ? want : cap);
+    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();
 }
 

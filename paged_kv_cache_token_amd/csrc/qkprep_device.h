@@ -42,6 +42,18 @@ __device__ __forceinline__ float4 ldf4(const float* p) {
     return *reinterpret_cast<const float4*>(p);
 }
 
+// Touch every dword of a kernel-argument struct at kernel entry.  The
+// compiler otherwise loads each field from the kernarg segment where it is
+// first used, and on a fresh launch each of those scalar loads misses: a
+// kernel whose phases use different fields pays one memory round trip per
+// phase.  Forcing all fields into SGPRs at entry turns that into one burst.
+template <typename T>
+__device__ __forceinline__ void preload_kernargs(const T& args) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&args);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(w[i]));
+}
+
 // ---------------------------------------------------------------------------
 // bf16 <-> fp32
 // ---------------------------------------------------------------------------

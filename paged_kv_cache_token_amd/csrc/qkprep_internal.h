@@ -61,6 +61,7 @@ struct NraDevArgs {
     int32_t tokens_per_tile;            // most tokens staged in LDS at once
     int32_t chunks_per_token;           // ceil(R / head rows per wave)
     int64_t total_items;                // T * chunks_per_token
+    int32_t grid;                       // workgroups launched (set by the launcher)
 };
 
 struct MlaDevArgs {
@@ -85,6 +86,7 @@ struct MlaDevArgs {
     int32_t tokens_per_tile;
     int32_t chunks_per_token;           // ceil(H / heads per wave) + 1 latent chunk
     int32_t n_tiles;
+    int32_t grid;                       // workgroups launched (set by the launcher)
 };
 
 // returns hipSuccess or the launch error
