@@ -96,12 +96,7 @@ __device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const
         sum += rp.count;
     }
     const int lane = tid & 63, wave = tid >> 6;
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int up = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += up;
-    }
+    const int incl = wave_inclusive_scan(sum);
     if (lane == 63) s_wave[wave] = incl;
     __syncthreads();
     int base = 0;
@@ -290,6 +285,7 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     __shared__ int64_t s_voff[kMaxTokensPerTile];
     __shared__ int64_t s_qsoff[kMaxTokensPerTile];
     __shared__ int s_tail[kTailPrefetch];
+    __shared__ int s_flag[4];
 
     preload_kernargs(a);
     const int tid = threadIdx.x;
@@ -363,13 +359,16 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     // request lookup, page and cos/sin row of every tile token (needs s_pos)
     auto stage_rows = [&]() {
         if (a.paged && tid < ntok) {
+            // indices are clamped so that malformed metadata (rejected by the
+            // verdict computed alongside) still reads inside the page table
             const int t = t_first + tid;
-            const int b = lds_upper_bound(s_indptr, a.B + 1, t) - 1;
+            const int b = min(max(lds_upper_bound(s_indptr, a.B + 1, t) - 1, 0), a.B - 1);
             const int beg = s_indptr[b];
             const int ql = s_indptr[b + 1] - beg;
             const int j = t - beg;
             const int L = s_seqlen[b] - ql + j;
-            const int64_t page = a.page_table[(int64_t)b * a.maxp + L / a.page_size];
+            const int pidx = min(max(L / a.page_size, 0), a.maxp - 1);
+            const int64_t page = a.page_table[(int64_t)b * a.maxp + pidx];
             const int64_t row = L % a.page_size;
             s_koff[tid] = page * a.k_page_stride + row * row_elems;
             s_voff[tid] = page * a.v_page_stride + row * row_elems;
@@ -390,10 +389,18 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
         const int b = r_lo + tid;
         if (tid < kTailPrefetch && b < r_hi) {
             const int sl = s_seqlen[b];
-            s_tail[tid] = (a.zero_tail && sl > 0)
-                              ? a.page_table[(int64_t)b * a.maxp + (sl - 1) / a.page_size] : -1;
+            const int pidx = min(max((sl - 1) / a.page_size, 0), a.maxp - 1);
+            s_tail[tid] = (a.zero_tail && sl > 0) ? a.page_table[(int64_t)b * a.maxp + pidx] : -1;
         }
     };
+
+    // device scalars of the call, loaded with the first round of metadata
+    RowConsts kc;
+    kc.inv_k = KVFP8 ? 1.0f / *a.k_scale : 1.0f;
+    kc.inv_v = KVFP8 ? 1.0f / *a.v_scale : 1.0f;
+    kc.q_static = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
+    kc.inv_um = (QMODE == 1) ? 1.0f / a.upper_max : 1.0f;
+    kc.qs_hstride = a.q_scale_padded ? (int)a.q_scale_P : 1;
 
     // ---- first tile: its qkv loads go out before the metadata chain ----
     const bool have_items = blo < bhi;
@@ -412,11 +419,13 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     if (have_items) stage_positions();
     __syncthreads();
     int bad = 0;
-    if (a.paged) bad = __syncthreads_or(validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave));
-    if (!bad) {
-        // With every request consistent, page-table reads stay inside each
-        // request's row.  The page-id checks, the tile's row lookups and cos/sin
-        // loads and the tail-page prefetch are independent: all issue at once.
+    if (a.paged) bad = validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave);
+    {
+        // The page-id checks, the tile's row lookups and cos/sin loads and the
+        // tail-page prefetch are independent and all issue at once.  Page
+        // reads stay inside the page table even for malformed metadata (the
+        // page counts of an inconsistent request are zero and the row lookups
+        // are clamped); nothing is written unless the whole call is valid.
         int p_first = 0;
         const int total_pages = a.paged ? s_pre[a.B] : 0;
         if (tid < total_pages) p_first = page_id_at(a, s_indptr, s_seqlen, s_pre, tid);
@@ -426,14 +435,8 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
         for (int k = tid + kBlockThreads; k < total_pages; k += kBlockThreads)
             bad |= page_out_of_pool(a, page_id_at(a, s_indptr, s_seqlen, s_pre, k));
     }
-    bad = __syncthreads_or(bad);
+    bad = block_or4(bad, s_flag);
 
-    RowConsts kc;
-    kc.inv_k = KVFP8 ? 1.0f / *a.k_scale : 1.0f;
-    kc.inv_v = KVFP8 ? 1.0f / *a.v_scale : 1.0f;
-    kc.q_static = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
-    kc.inv_um = (QMODE == 1) ? 1.0f / a.upper_max : 1.0f;
-    kc.qs_hstride = a.q_scale_padded ? (int)a.q_scale_P : 1;
 
     auto run_batch = [&](uint4 (&buf)[U][2]) {
 #pragma unroll

@@ -147,6 +147,33 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// wave and block primitives
+// ---------------------------------------------------------------------------
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: Hillis-Steele
+// inside each row of 16 lanes (row_shr 1, 2, 4, 8), then the row totals are
+// carried across rows with row_bcast:15 (into rows 1 and 3) and row_bcast:31
+// (into rows 2 and 3).
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+// OR of `v` over the workgroup (4 waves) with a single barrier; `slot` is
+// 4 ints of LDS used by this call site only.
+__device__ __forceinline__ int block_or4(int v, int* slot) {
+    const bool any = __ballot(v != 0) != 0;
+    if ((threadIdx.x & 63) == 0) slot[threadIdx.x >> 6] = any ? 1 : 0;
+    __syncthreads();
+    return slot[0] | slot[1] | slot[2] | slot[3];
+}
+
+// ---------------------------------------------------------------------------
 // one 16-byte store per lane for an FP8 head row
 // ---------------------------------------------------------------------------
 

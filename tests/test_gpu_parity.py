@@ -307,3 +307,36 @@ def test_graph_capture_replays_match_eager():
         got = _snapshot(dev)
         for a, b in zip(eager, got):
             assert torch.equal(a, b), f"replay {rep} differs from eager"
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_every_written_page_is_checked(seed):
+    """Corrupt one randomly chosen page id among those the call writes (many
+    requests, several pages each, so the flattened page checks span several
+    waves): the call must be rejected.  Then corrupt an id the call does not
+    touch: the call must go through."""
+    rng = np.random.default_rng(seed)
+    B = 300
+    q = rng.integers(0, 40, size=B)
+    prior = rng.integers(0, 200, size=B)
+    base = W.nra_case(seed=seed, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=4, maxp=100)
+    for trial in range(6):
+        inp = W.nra_case(seed=seed, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=4, maxp=100)
+        b = int(rng.integers(0, B))
+        sl, ql = int(inp.seq_lens[b]), int(q[b])
+        lo = sl - ql if ql > 0 else sl - 1
+        if sl <= 0 or sl <= lo:
+            continue
+        k = int(rng.integers(lo // 4, (sl - 1) // 4 + 1))
+        inp.page_table[b, k] = inp.num_pages + int(rng.integers(0, 5))
+        dev = H.DeviceNra(inp)
+        dev.run()
+        torch.cuda.synchronize()
+        gpu = dev.host_outputs()
+        assert (gpu["flags"] == -1).all(), (b, k)
+        H.check_exact(gpu["k_cache"], inp.k_cache0, "k_cache")
+    # an untouched page-table entry may hold anything
+    inp = base
+    b = int(np.argmax(inp.seq_lens > 8))
+    inp.page_table[b, 0] = -7 if (int(inp.seq_lens[b]) - int(q[b])) >= 4 else inp.page_table[b, 0]
+    run_and_compare(inp)
