@@ -12,15 +12,18 @@ region starts.  `value` is the step's algorithmic bytes (qkv read + norm
 weights + cos/sin rows + Q write incl. q_scale + cache write incl. tail
 zeros) divided by the measured step time, in GB/s (1e9 B/s).
 
-Also reported: tokens/s, the roofline of the dominant kernel (the prefill
-launch, timed one launch at a time with HIP events on its stream after an
-L2/MALL flush), and the CPU oracle timed on the host on the same step.
+Also reported: tokens/s; per-kernel durations from HIP events recorded on
+the launch stream around every launch of the timed region (the roofline of
+the dominant kernel, the prefill launch, uses their average); the same
+launches timed one at a time after a clean 512 MiB read flush of L2 and the
+256 MB Infinity Cache; and the CPU oracle timed on the host on the same step.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -48,6 +51,8 @@ def parse():
     ap.add_argument("--no-roofline", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "mla"], default=None,
                     help="time one workload alone (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB copy (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -98,12 +103,16 @@ class Call:
             q_scale_layout=qp.QSCALE_REQ_HEAD_PADDED if inp.q_scale_padded else qp.QSCALE_TOKEN_HEAD,
             max_seqlen=inp.max_seqlen, upper_max=inp.upper_max, flags=self.flags)
         self.params = qp.norm_rope_append_params(**self.kw)
+        self.params.struct_size = ctypes.sizeof(self.params)
+        self._ref = ctypes.byref(self.params)
+        self._fn = qp.lib().qkprep_norm_rope_append
+        self._stream = torch.cuda.current_stream().cuda_stream
         self.bytes = inp.algorithmic_bytes()["total"]
 
-    def launch(self, stream=None):
-        import paged_kv_cache_token_amd as qp
-        st = qp.call_norm_rope_append(self.params, stream)
+    def launch(self):
+        st = self._fn(self._ref, self._stream)
         if st != 0:
+            import paged_kv_cache_token_amd as qp
             raise qp.QkprepError(st)
 
 
@@ -123,11 +132,14 @@ class MlaCall:
             cos_sin_cache=up(inp.cos_sin, torch.float32), positions=up(inp.positions, torch.int64),
             slot_mapping=up(inp.slot_mapping, torch.int64), kv_cache=self.cache, num_q_heads=inp.H,
             kv_scale=torch.tensor([inp.kv_scale], dtype=torch.float32, device=dev))
+        self.params.struct_size = ctypes.sizeof(self.params)
+        self._ref = ctypes.byref(self.params)
+        self._fn = qp.lib().qkprep_mla_concat_rope_append
+        self._stream = torch.cuda.current_stream().cuda_stream
         self.bytes = inp.algorithmic_bytes()["total"]
 
-    def launch(self, stream=None):
-        import paged_kv_cache_token_amd as qp
-        st = qp.call_mla_concat_rope_append(self.params, stream)
+    def launch(self):
+        st = self._fn(self._ref, self._stream)
         if st != 0:
             raise qp.QkprepError(st)
 
@@ -200,6 +212,22 @@ def cpu_baseline(c2, c3):
                       "single-threaded C oracle in fp64"}
 
 
+def copy_calibration(dev):
+    """A plain copy of known size (256 MiB), for scaling the FETCH_SIZE /
+    WRITE_SIZE counters: run under rocprofv3 --pmc, each dispatch must read
+    and write 262144 KiB."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        flush.sum()
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -210,46 +238,61 @@ def main():
     import paged_kv_cache_token_amd as qp  # noqa: F401  (fails loudly if libqkprep.so is missing)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
 
     log("generating decode B=256")
     c2 = Call(W.c2_decode_b256(), dev)
     log("generating ragged FP8 prefill")
     c3 = Call(W.c3_prefill_fp8(), dev)
-    calls = {"decode": [c2], "prefill": [c3]}
+    calls = {"decode": c2, "prefill": c3}
     if args.only == "mla":
-        calls = {"mla": [MlaCall(W.c5_mla(), dev)]}
+        calls = {"mla": MlaCall(W.c5_mla(), dev)}
     elif args.only:
         calls = {args.only: calls[args.only]}
-    step_calls = [c for v in calls.values() for c in v]
+    names = list(calls)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        for c in step_calls:
+        for c in calls.values():
             c.launch()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
+    # events around every launch of the timed region, on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        for c in step_calls:
-            c.launch()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        for i, name in enumerate(names):
+            calls[name].launch()
+            ev[k][i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    step_bytes = sum(c.bytes for c in step_calls)
-    step_tokens = sum(c.inp.T for c in step_calls)
+    step_bytes = sum(c.bytes for c in calls.values())
+    step_tokens = sum(c.inp.T for c in calls.values())
     value = step_bytes / (ms * 1e-3) / 1e9
 
-    # per-launch times on the launch stream, each after a cache flush
     breakdown = {}
-    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
-    dominant = None
+    for i, name in enumerate(names):
+        c = calls[name]
+        durs = sorted(ev[k][i].elapsed_time(ev[k][i + 1]) * 1e3 for k in range(args.steps))
+        avg = sum(durs) / len(durs)
+        breakdown[name] = {"tokens": c.inp.T, "algorithmic_bytes": c.bytes, "avg_us": round(avg, 2),
+                           "median_us": round(durs[len(durs) // 2], 2),
+                           "GBps": round(c.bytes / (avg * 1e-6) / 1e9, 1),
+                           "Mtok_per_s": round(c.inp.T / avg, 2)}
+    # the same launches one at a time after a clean flush (512 MiB read)
     if not args.no_roofline:
-        for name, cl in calls.items():
-            c = cl[0]
+        flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        for name in names:
+            c = calls[name]
             durs = []
-            for i in range(args.roofline_launches):
-                flush.fill_(i & 0xFF)
+            for _ in range(args.roofline_launches):
+                flush.sum()
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
@@ -258,25 +301,20 @@ def main():
                 torch.cuda.synchronize()
                 durs.append(e0.elapsed_time(e1) * 1e3)
             durs.sort()
-            avg = sum(durs) / len(durs)
-            breakdown[name] = {"tokens": c.inp.T, "algorithmic_bytes": c.bytes, "avg_us": round(avg, 2),
-                               "median_us": round(durs[len(durs) // 2], 2),
-                               "GBps": round(c.bytes / (avg * 1e-6) / 1e9, 1),
-                               "Mtok_per_s": round(c.inp.T / avg, 2)}
-            if dominant is None or breakdown[name]["avg_us"] > breakdown[dominant]["avg_us"]:
-                dominant = name
-    del flush
+            med = durs[len(durs) // 2]
+            breakdown[name]["clean_cache_median_us"] = round(med, 2)
+            breakdown[name]["clean_cache_GBps"] = round(c.bytes / (med * 1e-6) / 1e9, 1)
+        del flush
+    dominant = max(names, key=lambda n: breakdown[n]["avg_us"])
     log(f"step {ms:.4f} ms, {value:.1f} GB/s; {breakdown}")
 
-    roofline = None
-    if dominant is not None:
-        b = breakdown[dominant]
-        khash = kernel_source_hash()
-        traffic = recorded_traffic(khash) if dominant == "prefill" else None
-        roofline = {"bound": "hbm", "kernel": dominant, "achieved": b["GBps"], "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(b["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "algorithmic_bytes_per_launch": b["algorithmic_bytes"], "avg_launch_us": b["avg_us"],
-                    "kernel_source_hash": khash}
+    b = breakdown[dominant]
+    khash = kernel_source_hash()
+    traffic = recorded_traffic(khash) if dominant == "prefill" else None
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": b["GBps"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(b["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": b["algorithmic_bytes"], "avg_launch_us": b["avg_us"],
+                "kernel_source_hash": khash}
 
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
@@ -291,8 +329,7 @@ def main():
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "config": {"workload": "decode B=256 (32/8/128 bf16, page 16, full pool) + ragged FP8 prefill "
                                f"(8 req, T={c3.inp.T}, 64/8/128, page 64)",
-                   "step_tokens": step_tokens, "step_algorithmic_bytes": step_bytes,
-                   "calls": list(calls)},
+                   "step_tokens": step_tokens, "step_algorithmic_bytes": step_bytes, "calls": names},
         "roofline": roofline, "cpu_baseline": cpu, "breakdown": breakdown,
     }
     print(json.dumps(out), flush=True)

@@ -11,26 +11,28 @@
 //    16 for D=256).  Lane l of the group loads two 16-byte vectors: elements
 //    [8l, 8l+8) and [D/2 + 8l, D/2 + 8l + 8).  Every NeoX pair (i, i + D/2)
 //    and every interleaved pair (2i, 2i+1) then sits in one lane's registers:
-//    RoPE needs no LDS and no lane exchange.  A wave covers 64/G head rows.
+//    RoPE needs no LDS and no lane exchange.  A wave covers 64/G head rows of
+//    one token (a "chunk").
 //  * The sum of squares and the FP8 amax are reduced over the G lanes of the
 //    row only (DPP within the lane group), never across rows or tokens.
-//  * The cos/sin values of a token are loaded straight into the registers of
-//    the lanes that use them (each lane needs exactly the 16 values of its
-//    own dims) and reused for every head row of that token the wave
-//    processes; no LDS staging is needed for them.
-//  * Work is cut into tiles.  A token tile holds `tokens_per_tile`
-//    consecutive tokens; its (token, chunk of 64/G head rows) items are
-//    split into 4 contiguous runs, one per wave, so a wave usually keeps one
-//    token's cos/sin for several chunks.  A request tile clears the tails of
-//    its requests' last pages and writes their flags.  The grid is
-//    persistent: workgroup w takes tiles w, w + a.grid, ...
+//  * Every workgroup owns a balanced, contiguous range of the (token, chunk)
+//    items and of the requests; the grid is sized to what stays resident.
+//    Tiles of up to 16 tokens stage their cos/sin rows, positions and cache
+//    row offsets in LDS; the norm weights are staged once per workgroup.
+//  * Loads are double-buffered and unconditional (rows past the run are
+//    clamped to a valid row) so that the wait for one batch never drains the
+//    loads of the next one.
 //  * All-or-nothing validation without a host sync or a second kernel:
 //    every workgroup stages q_indptr / seq_lens in LDS, checks every request
-//    and every page id the call will write (the pages are enumerated
-//    through a block-wide prefix sum so each thread checks ~1 page), and
-//    reduces the verdict with a barrier.  Every workgroup reads the same
-//    metadata, so all reach the same verdict.  An invalid call leaves every
-//    token tile idle and makes the request tiles write -1 flags.
+//    and every page id the call will write (the pages are enumerated through
+//    a wave prefix sum so each thread checks about one page), and reduces the
+//    verdict with one barrier.  Every workgroup reads the same metadata, so
+//    all reach the same verdict.  An invalid call makes the workgroups write
+//    -1 flags and nothing else.
+//  * The latency chain of a small call is kept at two dependent memory
+//    rounds: the first batch of qkv loads leaves at kernel entry, and the
+//    page checks, row lookups, cos/sin rows and tail pages all issue in the
+//    round after the request metadata arrives.
 #include <type_traits>
 
 #include "qkprep_device.h"
@@ -136,6 +138,7 @@ struct KvType {
 struct RowConsts {
     float inv_k, inv_v, q_static, inv_um;
     int qs_hstride;
+    float* s_qs;     // non-null: stage dynamic Q scales in LDS [token][head]
 };
 
 template <int D, int QMODE, bool KVFP8>
@@ -230,7 +233,10 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
                 // s = max(amax, 1e-6) / upper_max; payload = x * (1 / s)
                 const float sc = __builtin_fmaxf(amax, 1e-6f) * k.inv_um;
                 mul = __builtin_amdgcn_rcpf(sc);
-                if (gl == 0) a.q_scale[s_qsoff[ti] + (int64_t)h * k.qs_hstride] = sc;
+                if (gl == 0) {
+                    if (k.s_qs) k.s_qs[ti * a.Hq + h] = sc;
+                    else a.q_scale[s_qsoff[ti] + (int64_t)h * k.qs_hstride] = sc;
+                }
             }
             store_fp8_row(dst - 8 * gl, gl, HALF, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
         }
@@ -276,7 +282,8 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     constexpr int D4 = D / 4;        // float4 per cos/sin row
     typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
 
-    extern __shared__ int s_dyn[];   // q_indptr [B+1] | seq_lens [B] | page prefix [B+1]
+    // q_indptr [B+1] | seq_lens [B] | page prefix [B+1] | (padded q_scale) staged scales [TPB][Hq]
+    extern __shared__ int s_dyn[];
     __shared__ int s_wave[4];
     __shared__ __align__(16) float s_w[2 * D];                       // q | k norm weights
     __shared__ __align__(16) float s_cs[kMaxTokensPerTile * D];      // cos/sin rows of the tile
@@ -401,6 +408,11 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     kc.q_static = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
     kc.inv_um = (QMODE == 1) ? 1.0f / a.upper_max : 1.0f;
     kc.qs_hstride = a.q_scale_padded ? (int)a.q_scale_P : 1;
+    // Padded scales of consecutive tokens are 4-byte neighbours in each head's
+    // row: written one by one they cost a partial-sector memory write each,
+    // so they are gathered per tile in LDS and written as contiguous runs.
+    kc.s_qs = (QMODE == 1 && a.stage_q_scale)
+                  ? reinterpret_cast<float*>(s_dyn + ((3 * a.B + 2 + 3) & ~3)) : nullptr;
 
     // ---- first tile: its qkv loads go out before the metadata chain ----
     const bool have_items = blo < bhi;
@@ -488,6 +500,22 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
                 load_batch(bufA);
                 run_batch(bufB);
             }
+            if (kc.s_qs) {
+                // each head's scales of the tile's tokens, token-contiguous;
+                // only the heads whose chunks lie in this workgroup's range
+                // (the first and last token may be shared with a neighbour)
+                __syncthreads();
+                const int c_first = sub_lo - t_first * CPT;            // first chunk of token 0
+                const int c_last = sub_hi - (t_first + ntok - 1) * CPT; // end chunk of the last token
+                for (int k = tid; k < ntok * a.Hq; k += kBlockThreads) {
+                    const int h = k / ntok;
+                    const int i = k - h * ntok;
+                    const int c = h / RPW;
+                    const bool mine = (i > 0 || c >= c_first) && (i < ntok - 1 || c < c_last);
+                    if (mine && s_pos[i] >= 0)
+                        a.q_scale[s_qsoff[i] + (int64_t)h * a.q_scale_P] = kc.s_qs[i * a.Hq + h];
+                }
+            }
             sub_lo = sub_hi;
             if (sub_lo >= bhi) break;
             __syncthreads();   // every wave is done with this tile's LDS rows
@@ -527,7 +555,8 @@ int resident_blocks(size_t lds) {
 
 template <int D, int QMODE, bool KVFP8>
 hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
-    const size_t lds = a.paged ? (size_t)(3 * a.B + 2) * sizeof(int) : 0;
+    size_t lds = a.paged ? (size_t)(3 * a.B + 2) * sizeof(int) : 0;
+    if (a.stage_q_scale) lds = (size_t)((3 * a.B + 2 + 3) & ~3) * sizeof(int) + (size_t)kMaxTokensPerTile * a.Hq * sizeof(float);
     // enough workgroups to fill every CU, none with less than 8 head-row
     // chunks of work, and at least one per 4 requests for the tail clears
     const int64_t cap = resident_blocks<D, QMODE, KVFP8>(lds);

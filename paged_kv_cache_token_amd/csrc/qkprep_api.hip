@@ -144,6 +144,7 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     a.q_scale_padded = padded ? 1 : 0;
     a.max_seqlen = p->max_seqlen;
     a.q_scale_P = padded ? ((int64_t)p->max_seqlen + 127) / 128 * 128 : 0;
+    a.stage_q_scale = padded && Hq <= kMaxStagedQHeads ? 1 : 0;
     a.q_scale_inv = p->q_scale_inv;
     a.upper_max = p->upper_max;
     a.k_out = static_cast<uint16_t*>(p->k_out);

@@ -13,6 +13,8 @@ namespace qkprep {
 constexpr int kMaxRequests = 4096;
 constexpr int kBlockThreads = 256;
 constexpr int kMaxTokensPerTile = 16;
+// largest Hq whose per-tile padded Q scales are gathered in LDS
+constexpr int kMaxStagedQHeads = 256;
 // head rows each wave has in flight per load batch (double-buffered)
 constexpr int kBatch = 2;
 // tail pages of the first requests a workgroup clears, prefetched with the metadata
@@ -51,6 +53,7 @@ struct NraDevArgs {
     int32_t q_scale_padded;
     int32_t max_seqlen;
     int64_t q_scale_P;                  // padded row length round_up(max_seqlen, 128)
+    int32_t stage_q_scale;              // gather padded scales per tile in LDS
     const float* q_scale_inv;
     float upper_max;
     uint16_t* k_out;
