@@ -9,13 +9,17 @@
 //  * The 64-element rope slice of one q head (128 bytes) is owned by 4 lanes.
 //    Lane l loads elements [8l, 8l+8) and [32 + 8l, 32 + 8l + 8); NeoX pairs
 //    (i, i + 32) and interleaved pairs (2i, 2i+1) are then both lane-local.
-//    A wave covers 16 heads; the nope part of q is never touched.
-//  * Per token: ceil(H / 16) q chunks plus one latent chunk in which the 64
-//    lanes convert 8 latent elements each (512 per pass) and lanes 0..3
-//    rotate and convert k_pe.  cos/sin live in the registers of the lanes
-//    that use them.
-//  * Tiles of `tokens_per_tile` tokens, items split into 4 contiguous runs,
-//    persistent grid.
+//    A wave covers 16 heads (a "q chunk"); the nope part of q is never read.
+//  * Per token: ceil(H / 16) q chunks plus one latent chunk.  In the latent
+//    chunk each of the 64 lanes loads 8 latent elements (512 per pass) and
+//    lanes 0..7 load the 64 k_pe elements; lanes 0..3 take the second half
+//    of k_pe from lanes 4..7, rotate it and convert it.
+//  * Every chunk issues exactly two 16-byte loads per lane, so the loads of
+//    the next two chunks are issued before the stores of the current ones
+//    with exact wait counts (double buffering).
+//  * Every workgroup owns a balanced, contiguous range of the (token, chunk)
+//    items; tiles of up to 16 tokens stage their cos/sin rows (64 floats),
+//    positions and cache-row offsets in LDS.
 #include <type_traits>
 
 #include "qkprep_device.h"
@@ -49,8 +53,41 @@ __device__ __forceinline__ void rope16(float* x, const float* c, const float* s,
     }
 }
 
+// the 16 cos/sin values lane gl of a head needs, from the LDS row of its token
+__device__ __forceinline__ void lane_cos_sin(const float* row, int gl, int style, float* c, float* s) {
+    float4 c0, c1, s0, s1;
+    if (style == 0) {
+        c0 = *reinterpret_cast<const float4*>(row + 8 * gl);
+        c1 = *reinterpret_cast<const float4*>(row + 8 * gl + 4);
+        s0 = *reinterpret_cast<const float4*>(row + kHalf + 8 * gl);
+        s1 = *reinterpret_cast<const float4*>(row + kHalf + 8 * gl + 4);
+    } else {
+        c0 = *reinterpret_cast<const float4*>(row + 4 * gl);
+        c1 = *reinterpret_cast<const float4*>(row + kRope / 4 + 4 * gl);
+        s0 = *reinterpret_cast<const float4*>(row + kHalf + 4 * gl);
+        s1 = *reinterpret_cast<const float4*>(row + kHalf + kRope / 4 + 4 * gl);
+    }
+    c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
+    c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
+    s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
+    s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
+}
+
+struct MlaCursor {
+    int t, c, left;
+    __device__ __forceinline__ void advance(int cpt) {
+        const bool wrap = c + 1 == cpt;
+        c = wrap ? 0 : c + 1;
+        t += wrap ? 1 : 0;
+        --left;
+    }
+};
+
 template <bool KVFP8>
 __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) {
+    constexpr int U = kBatch;
+    typedef typename std::conditional<KVFP8, uint8_t, uint16_t>::type kv_t;
+    __shared__ __align__(16) float s_cs[kMaxTokensPerTile * kRope];
     __shared__ int s_pos[kMaxTokensPerTile];
     __shared__ int64_t s_row[kMaxTokensPerTile];   // element offset of the cache row, -1 = skip
 
@@ -62,112 +99,181 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     const int gl = lane % kLanesPerHead;
     const int K = a.kv_lora_rank;
     const int row_len = K + kRope;
-    const int n_qchunks = a.chunks_per_token - 1;
+    const int CPT = a.chunks_per_token;
+    const int n_qchunks = CPT - 1;
     const int TPB = a.tokens_per_tile;
     const float inv_scale = KVFP8 ? 1.0f / *a.kv_scale : 1.0f;
-
-    typedef typename std::conditional<KVFP8, uint8_t, uint16_t>::type kv_t;
     kv_t* cache = reinterpret_cast<kv_t*>(a.kv_cache);
 
-    for (int tile = blockIdx.x; tile < a.n_tiles; tile += a.grid) {
-        const int t0 = tile * TPB;
-        if (tid < TPB) {
-            const int t = t0 + tid;
-            int pos = -1;
-            int64_t row = -1;
-            if (t < a.T) {
-                const int64_t p64 = a.positions[t];
-                if (p64 >= 0 && p64 < a.cs_rows) pos = (int)p64;
-                const int64_t slot = a.slot_mapping[t];
-                if (slot >= 0 && slot < a.capacity)
-                    row = (slot / a.block_size) * a.block_stride + (slot % a.block_size) * (int64_t)row_len;
-            }
-            s_pos[tid] = pos;
-            s_row[tid] = row;
-        }
-        __syncthreads();
+    const int blo = (int)((int64_t)a.total_items * blockIdx.x / a.grid);
+    const int bhi = (int)((int64_t)a.total_items * (blockIdx.x + 1) / a.grid);
+    int sub_lo = blo, sub_hi = blo, t_first = 0, ntok = 0;
+    MlaCursor ld{0, 0, 0}, pr{0, 0, 0};
+    uint4 bufA[U][2], bufB[U][2];
 
-        const int n_items = TPB * a.chunks_per_token;
-        const int ipw = (n_items + 3) >> 2;
-        const int it_lo = wave * ipw;
-        const int it_hi = min(n_items, it_lo + ipw);
-        int cur_ti = -1;
-        float c[8], s[8];
-        for (int it = it_lo; it < it_hi; ++it) {
-            const int ti = it / a.chunks_per_token;
-            const int chunk = it - ti * a.chunks_per_token;
-            const int t = t0 + ti;
-            if (t >= a.T) break;
-            const int pos = s_pos[ti];
-            if (pos < 0) continue;
-            if (ti != cur_ti) {
-                cur_ti = ti;
-                const float* cs = a.cos_sin + (int64_t)pos * kRope;
-                float4 c0, c1, s0, s1;
-                if (a.rope == 0) {
-                    c0 = ldf4(cs + 8 * gl); c1 = ldf4(cs + 8 * gl + 4);
-                    s0 = ldf4(cs + kHalf + 8 * gl); s1 = ldf4(cs + kHalf + 8 * gl + 4);
-                } else {
-                    c0 = ldf4(cs + 4 * gl); c1 = ldf4(cs + kRope / 4 + 4 * gl);
-                    s0 = ldf4(cs + kHalf + 4 * gl); s1 = ldf4(cs + kHalf + kRope / 4 + 4 * gl);
-                }
-                c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w;
-                c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
-                s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w;
-                s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
+    // two 16-byte loads per lane per chunk, always issued (clamped rows)
+    auto load_batch = [&](uint4 (&buf)[U][2]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = ld.left > 0 ? ld.t : t_first;
+            const uint16_t* p0;
+            const uint16_t* p1;
+            if (ld.c < n_qchunks) {
+                const int h0 = ld.c * kHeadsPerWave + grp;
+                const int h = h0 < a.H ? h0 : 0;
+                p0 = a.q + (int64_t)t * a.q_token_stride + (int64_t)h * a.q_head_stride + a.nope_dim + 8 * gl;
+                p1 = p0 + kHalf;
+            } else {
+                p0 = a.kv_c + (int64_t)t * a.kv_c_stride + 8 * lane;
+                p1 = a.k_pe + (int64_t)t * a.k_pe_stride + 8 * (lane & 7);
             }
-            if (chunk < n_qchunks) {
-                // ---- q rope slice of head h, in place ----
-                const int h = chunk * kHeadsPerWave + grp;
-                if (h >= a.H) continue;
-                uint16_t* p = a.q + (int64_t)t * a.q_token_stride + (int64_t)h * a.q_head_stride +
-                              a.nope_dim + 8 * gl;
-                float x[16];
-                unpack8(ld16(p), x);
-                unpack8(ld16(p + kHalf), x + 8);
-                rope16(x, c, s, a.rope);
-                st16(p, pack8_bf16(x));
-                st16(p + kHalf, pack8_bf16(x + 8));
-                continue;
-            }
-            // ---- latent chunk: [kv_c | RoPE(k_pe)] -> cache row ----
-            const int64_t row = s_row[ti];
-            if (row < 0) continue;
-            kv_t* dst = cache + row;
-            const uint16_t* kc = a.kv_c + (int64_t)t * a.kv_c_stride;
-            for (int e = 8 * lane; e < K; e += 512) {
-                const uint4 v = ld16(kc + e);
-                if constexpr (KVFP8) {
-                    float x[8];
-                    unpack8(v, x);
-                    st8(dst + e, pack8_fp8(x, inv_scale));
+            buf[u][0] = ld16(p0);
+            buf[u][1] = ld16(p1);
+            ld.advance(CPT);
+        }
+    };
+    auto start_tile = [&]() {
+        t_first = sub_lo / CPT;
+        sub_hi = min(bhi, (t_first + TPB) * CPT);
+        ntok = (sub_hi - 1) / CPT - t_first + 1;
+        const int n = sub_hi - sub_lo;
+        const int w_lo = sub_lo + n * wave / 4;
+        const int w_hi = sub_lo + n * (wave + 1) / 4;
+        ld.t = w_lo / CPT;
+        ld.c = w_lo - ld.t * CPT;
+        ld.left = w_hi - w_lo;
+        pr = ld;
+    };
+    auto stage_tile = [&]() {
+        if (tid < ntok) {
+            const int t = t_first + tid;
+            const int64_t p64 = a.positions[t];
+            const int64_t slot = a.slot_mapping[t];
+            s_pos[tid] = (p64 >= 0 && p64 < a.cs_rows) ? (int)p64 : -1;
+            s_row[tid] = (slot >= 0 && slot < a.capacity)
+                             ? (slot / a.block_size) * a.block_stride + (slot % a.block_size) * (int64_t)row_len
+                             : -1;
+        }
+        // cos/sin rows (positions read again: the LDS copy is not yet visible)
+        for (int k = tid; k < ntok * (kRope / 4); k += kBlockThreads) {
+            const int i = k / (kRope / 4);
+            const int c4 = k - i * (kRope / 4);
+            const int64_t p64 = a.positions[t_first + i];
+            if (p64 >= 0 && p64 < a.cs_rows)
+                *reinterpret_cast<float4*>(s_cs + i * kRope + 4 * c4) = ldf4(a.cos_sin + p64 * kRope + 4 * c4);
+        }
+    };
+    auto run_batch = [&](uint4 (&buf)[U][2]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (pr.left > 0) {
+                const int t = pr.t;
+                const int ti = t - t_first;
+                const int chunk = pr.c;
+                const int pos = s_pos[ti];
+                if (chunk < n_qchunks) {
+                    const int h = chunk * kHeadsPerWave + grp;
+                    if (pos >= 0 && h < a.H) {
+                        float c[8], s[8], x[16];
+                        lane_cos_sin(s_cs + ti * kRope, gl, a.rope, c, s);
+                        unpack8(buf[u][0], x);
+                        unpack8(buf[u][1], x + 8);
+                        rope16(x, c, s, a.rope);
+                        uint16_t* p = a.q + (int64_t)t * a.q_token_stride + (int64_t)h * a.q_head_stride +
+                                      a.nope_dim + 8 * gl;
+                        st16(p, pack8_bf16(x));
+                        st16(p + kHalf, pack8_bf16(x + 8));
+                    }
                 } else {
-                    st16(dst + e, v);
+                    // k_pe second halves come from lanes 4..7 (all lanes take part)
+                    const uint4 pe = buf[u][1];
+                    uint4 pe_hi;
+                    pe_hi.x = __shfl(pe.x, lane + 4, 64);
+                    pe_hi.y = __shfl(pe.y, lane + 4, 64);
+                    pe_hi.z = __shfl(pe.z, lane + 4, 64);
+                    pe_hi.w = __shfl(pe.w, lane + 4, 64);
+                    const int64_t row = s_row[ti];
+                    if (pos >= 0 && row >= 0) {
+                        kv_t* dst = cache + row;
+                        if constexpr (KVFP8) {
+                            float x[8];
+                            unpack8(buf[u][0], x);
+                            st8(dst + 8 * lane, pack8_fp8(x, inv_scale));
+                        } else {
+                            st16(dst + 8 * lane, buf[u][0]);
+                        }
+                        // latent ranks past the first 512 (kv_lora_rank = 1024, ...)
+                        for (int e = 512 + 8 * lane; e < K; e += 512) {
+                            const uint4 v = ld16(a.kv_c + (int64_t)t * a.kv_c_stride + e);
+                            if constexpr (KVFP8) {
+                                float x[8];
+                                unpack8(v, x);
+                                st8(dst + e, pack8_fp8(x, inv_scale));
+                            } else {
+                                st16(dst + e, v);
+                            }
+                        }
+                        if (lane < kLanesPerHead) {
+                            float c[8], s[8], x[16];
+                            lane_cos_sin(s_cs + ti * kRope, gl, a.rope, c, s);
+                            unpack8(pe, x);
+                            unpack8(pe_hi, x + 8);
+                            rope16(x, c, s, a.rope);
+                            if constexpr (KVFP8) {
+                                store_fp8_row(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf, pack8_fp8(x, inv_scale),
+                                              pack8_fp8(x + 8, inv_scale));
+                            } else {
+                                st16(dst + K + 8 * gl, pack8_bf16(x));
+                                st16(dst + K + kHalf + 8 * gl, pack8_bf16(x + 8));
+                            }
+                        }
+                    }
                 }
-            }
-            if (lane < kLanesPerHead) {
-                const uint16_t* kp = a.k_pe + (int64_t)t * a.k_pe_stride + 8 * gl;
-                float x[16];
-                unpack8(ld16(kp), x);
-                unpack8(ld16(kp + kHalf), x + 8);
-                rope16(x, c, s, a.rope);
-                if constexpr (KVFP8) {
-                    store_fp8_row(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf, pack8_fp8(x, inv_scale),
-                                  pack8_fp8(x + 8, inv_scale));
-                } else {
-                    st16(dst + K + 8 * gl, pack8_bf16(x));
-                    st16(dst + K + kHalf + 8 * gl, pack8_bf16(x + 8));
-                }
+                pr.advance(CPT);
             }
         }
+    };
+
+    for (bool first = true; sub_lo < bhi; first = false) {
+        if (!first) __syncthreads();   // every wave is done with the previous tile's LDS
+        start_tile();
+        load_batch(bufA);
+        stage_tile();
         __syncthreads();
+        while (pr.left > 0) {
+            load_batch(bufB);
+            run_batch(bufA);
+            if (pr.left <= 0) break;
+            load_batch(bufA);
+            run_batch(bufB);
+        }
+        sub_lo = sub_hi;
     }
+}
+
+template <bool KVFP8>
+int resident_blocks() {
+    static int cached_dev = -1, cached = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev != cached_dev) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mla_kernel<KVFP8>, kBlockThreads, 0) != hipSuccess)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+        cached = (per_cu < 1 ? 1 : per_cu) * cus;
+        cached_dev = dev;
+    }
+    return cached;
 }
 
 template <bool KVFP8>
 hipError_t launch_t(const MlaDevArgs& a, hipStream_t stream) {
     MlaDevArgs la = a;
-    la.grid = a.n_tiles < 8192 ? a.n_tiles : 8192;
+    const int64_t cap = resident_blocks<KVFP8>();
+    int64_t want = (a.total_items + 7) / 8;
+    if (want < 1) want = 1;
+    la.grid = (int)(want < cap ? want : cap);
     hipLaunchKernelGGL((mla_kernel<KVFP8>), dim3(la.grid), dim3(kBlockThreads), 0, stream, la);
     return hipGetLastError();
 }

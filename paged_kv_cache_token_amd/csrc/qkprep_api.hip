@@ -17,22 +17,6 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int gcd_int(int a, int b) {
-    while (b) { int t = a % b; a = b; b = t; }
-    return a;
-}
-
-// tokens per tile: enough (token, chunk) items to give the 4 waves equal
-// runs; longer runs for large calls so a wave keeps one token's cos/sin for
-// all of that token's chunks
-int tokens_per_tile(int T, int cpt) {
-    int tpb = 4 / gcd_int(cpt, 4);
-    if (T >= 4096) {
-        while (tpb * cpt / 4 < cpt && tpb * 2 <= kMaxTokensPerTile) tpb *= 2;
-    }
-    return tpb;
-}
-
 }  // namespace
 
 extern "C" {
@@ -200,8 +184,8 @@ qkprep_status qkprep_mla_concat_rope_append(const qkprep_mla_params* p, hipStrea
     a.block_size = p->block_size; a.block_stride = p->block_stride;
     a.kv_scale = p->kv_scale;
     a.chunks_per_token = (a.H + 15) / 16 + 1;
-    a.tokens_per_tile = tokens_per_tile(T, a.chunks_per_token);
-    a.n_tiles = (T + a.tokens_per_tile - 1) / a.tokens_per_tile;
+    a.tokens_per_tile = kMaxTokensPerTile;
+    a.total_items = (int64_t)T * a.chunks_per_token;
     hipError_t e = launch_mla_concat_rope(a, p->kv_dtype, stream);
     return e == hipSuccess ? QKPREP_OK : QKPREP_E_LAUNCH;
 }

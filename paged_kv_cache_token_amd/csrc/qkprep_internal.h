@@ -85,10 +85,10 @@ struct MlaDevArgs {
     int32_t block_size;
     int64_t block_stride;
     const float* kv_scale;
-    // geometry
-    int32_t tokens_per_tile;
+    // geometry: balanced contiguous ranges of the T * chunks_per_token items
+    int32_t tokens_per_tile;            // most tokens staged in LDS at once
     int32_t chunks_per_token;           // ceil(H / heads per wave) + 1 latent chunk
-    int32_t n_tiles;
+    int64_t total_items;
     int32_t grid;                       // workgroups launched (set by the launcher)
 };
 
