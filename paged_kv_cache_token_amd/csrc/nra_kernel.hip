@@ -307,12 +307,28 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     const int CPT = a.chunks_per_token;
     const int TPB = a.tokens_per_tile;
     const int64_t row_elems = (int64_t)a.Hkv * D;
-    const int blo = (int)((int64_t)a.total_items * blockIdx.x / a.grid);
-    const int bhi = (int)((int64_t)a.total_items * (blockIdx.x + 1) / a.grid);
+    // Item ranges of this workgroup: one balanced contiguous range, or (when
+    // a.interleave > 0) spans of a.interleave items dealt round-robin, so that
+    // the workgroups running at any moment read neighbouring parts of qkv.
+    int range_k = 0, blo = 0, bhi = 0;
+    auto next_range = [&]() -> bool {
+        if (a.interleave == 0) {
+            if (range_k++ > 0) return false;
+            blo = (int)((int64_t)a.total_items * blockIdx.x / a.grid);
+            bhi = (int)((int64_t)a.total_items * (blockIdx.x + 1) / a.grid);
+            return blo < bhi;
+        }
+        const int64_t tile = blockIdx.x + (int64_t)(range_k++) * a.grid;
+        const int64_t span = a.interleave;
+        if (tile * span >= a.total_items) return false;
+        blo = (int)(tile * span);
+        bhi = (int)min((int64_t)a.total_items, tile * span + span);
+        return true;
+    };
 
     uint4 bufA[U][2], bufB[U][2];
     Cursor ld{0, 0, 0}, pr{0, 0, 0};
-    int sub_lo = blo, t_first = 0, ntok = 0, sub_hi = blo;
+    int sub_lo = 0, t_first = 0, ntok = 0, sub_hi = 0;
     // Loads of the next U head rows of the wave's run (no metadata needed).
     // Always exactly 2 U loads, with rows past the run or past R clamped to a
     // valid row: the compiler's wait counters then stay exact, and a wait for
@@ -415,7 +431,8 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
                   ? reinterpret_cast<float*>(s_dyn + ((3 * a.B + 2 + 3) & ~3)) : nullptr;
 
     // ---- first tile: its qkv loads go out before the metadata chain ----
-    const bool have_items = blo < bhi;
+    const bool have_items = next_range();
+    sub_lo = blo;
     if (have_items) {
         start_tile();
         load_batch(bufA);
@@ -517,7 +534,10 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
                 }
             }
             sub_lo = sub_hi;
-            if (sub_lo >= bhi) break;
+            if (sub_lo >= bhi) {
+                if (!next_range()) break;
+                sub_lo = blo;
+            }
             __syncthreads();   // every wave is done with this tile's LDS rows
             start_tile();
             load_batch(bufA);
@@ -565,6 +585,12 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     if (want < 1) want = 1;
     NraDevArgs la = a;
     la.grid = (int)(want < cap ? want : cap);
+    // Long calls (8 or more tokens per workgroup) deal 4-token spans
+    // round-robin: the resident workgroups then stream through one window of
+    // qkv and the caches instead of the whole call at once, which keeps the
+    // HBM accesses of the moment close together (about 6 % faster on a
+    // 15k-token prefill).  Short calls keep one contiguous range each.
+    la.interleave = (a.T >= 8 * (int64_t)la.grid) ? 4 * a.chunks_per_token : 0;
     hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();
 }

@@ -64,6 +64,7 @@ struct NraDevArgs {
     int32_t tokens_per_tile;            // most tokens staged in LDS at once
     int32_t chunks_per_token;           // ceil(R / head rows per wave)
     int64_t total_items;                // T * chunks_per_token
+    int32_t interleave;                 // items per round-robin span, 0 = one range per workgroup
     int32_t grid;                       // workgroups launched (set by the launcher)
 };
 
