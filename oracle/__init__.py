@@ -66,6 +66,9 @@ def lib():
         L.oracle_rope.restype = None
         L.oracle_rope.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_rope_partial.restype = None
+        L.oracle_rope_partial.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.oracle_q_scale.restype = ctypes.c_float
         L.oracle_q_scale.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_double]
         L.oracle_norm_rope_append.restype = ctypes.c_int
@@ -119,12 +122,16 @@ def rmsnorm(x: np.ndarray, w: np.ndarray | None, norm: int, eps: float) -> np.nd
     return y
 
 
-def rope(y: np.ndarray, rope_style: int, c: np.ndarray, s: np.ndarray) -> np.ndarray:
+def rope(y: np.ndarray, rope_style: int, c: np.ndarray, s: np.ndarray, rot: int | None = None) -> np.ndarray:
+    """RoPE of one head row; ``rot`` rotated dims (default: the whole row)."""
     y = np.ascontiguousarray(y, dtype=np.float64)
     c = np.ascontiguousarray(c, dtype=np.float64)
     s = np.ascontiguousarray(s, dtype=np.float64)
     o = np.empty_like(y)
-    lib().oracle_rope(_ptr(y), y.size, rope_style, _ptr(c), _ptr(s), _ptr(o))
+    if rot is None:
+        lib().oracle_rope(_ptr(y), y.size, rope_style, _ptr(c), _ptr(s), _ptr(o))
+    else:
+        lib().oracle_rope_partial(_ptr(y), y.size, int(rot), rope_style, _ptr(c), _ptr(s), _ptr(o))
     return o
 
 
@@ -140,6 +147,7 @@ def q_scale(v32: np.ndarray, upper_max: float) -> float:
 class _NraArgs(ctypes.Structure):
     _fields_ = [
         ("T", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("rot", ctypes.c_int32),
         ("qkv", ctypes.c_void_p), ("qkv_row_stride", ctypes.c_int64),
         ("norm", ctypes.c_int32), ("eps", ctypes.c_float),
         ("q_w", ctypes.c_void_p), ("k_w", ctypes.c_void_p),
@@ -203,7 +211,7 @@ def norm_rope_append(inp, out) -> NraResult:
     v_cache = _need(out["v_cache"], np.uint8 if inp.kv_fp8 else np.uint16)
     D = inp.D
     a = _NraArgs()
-    a.T, a.Hq, a.Hkv, a.D = inp.T, inp.Hq, inp.Hkv, D
+    a.T, a.Hq, a.Hkv, a.D, a.rot = inp.T, inp.Hq, inp.Hkv, D, inp.rot
     a.qkv = _ptr(qkv)
     a.qkv_row_stride = inp.qkv_row_stride
     a.norm = inp.norm

@@ -32,8 +32,9 @@
  *
  * Readings where the pages are silent (each is listed in the design doc):
  *  - cos_sin_cache row p is [cos(p f_0) .. cos(p f_{R/2-1}) | sin(...)].
- *    NeoX pairs (i, i + D/2) use angle i; interleaved pairs (2i, 2i+1) use
- *    angle i.
+ *    NeoX pairs (i, i + R/2) use angle i; interleaved pairs (2i, 2i+1) use
+ *    angle i.  With R < D the first R dims of a head rotate and the rest
+ *    pass through; with R = 0 no dim rotates and positions are not read.
  *  - norm 0 = none, 1 = x * inv * w, 2 = x * inv * (1 + w).
  *  - The fused pass keeps full precision until the final store; the oracle
  *    keeps fp64, rounds the rotated value once to fp32 ("v32"), and encodes
@@ -182,14 +183,19 @@ void oracle_rmsnorm(const double *x, int D, const float *w, int norm, double eps
     }
 }
 
-/* Rotary embedding of one head row of length D with R = D rotated dims.
- * c[i], s[i] (i < D/2) are the cosine and sine of angle i.
- *   NeoX (rope 0):        pair (i, i + D/2)
+/* Rotary embedding of one head row of length D whose first R dims rotate
+ * (R even, 0 <= R <= D); dims [R, D) pass through unchanged (the partial
+ * rotary of the vLLM issue's model table: RoPE on part of the head, NoPE on
+ * the rest; R = 0 is a NoPE layer).  c[i], s[i] (i < R/2) are the cosine and
+ * sine of angle i.
+ *   NeoX (rope 0):        pair (i, i + R/2)
  *   interleaved (rope 1): pair (2i, 2i + 1)
  * For a pair (a, b):  a' = a c - b s,  b' = b c + a s. */
-void oracle_rope(const double *y, int D, int rope, const double *c, const double *s, double *o)
+void oracle_rope_partial(const double *y, int D, int R, int rope, const double *c, const double *s,
+                         double *o)
 {
-    int half = D / 2;
+    int half = R / 2;
+    for (int d = R; d < D; ++d) o[d] = y[d];
     for (int i = 0; i < half; ++i) {
         int ia = (rope == 0) ? i : 2 * i;
         int ib = (rope == 0) ? i + half : 2 * i + 1;
@@ -197,6 +203,12 @@ void oracle_rope(const double *y, int D, int rope, const double *c, const double
         o[ia] = a * c[i] - b * s[i];
         o[ib] = b * c[i] + a * s[i];
     }
+}
+
+/* The whole head rotates (R = D). */
+void oracle_rope(const double *y, int D, int rope, const double *c, const double *s, double *o)
+{
+    oracle_rope_partial(y, D, D, rope, c, s, o);
 }
 
 /* Dynamic per-(token, head) FP8 scale (FlashInfer "What changes"):
@@ -217,8 +229,8 @@ float oracle_q_scale(const float *v, int D, double upper_max)
 /* ------------------------------------------------------------------ */
 
 typedef struct {
-    /* shapes */
-    int32_t T, Hq, Hkv, D;
+    /* shapes; rot = rotated dims per head (even, 0..D) */
+    int32_t T, Hq, Hkv, D, rot;
     /* qkv: bf16 bits, row t at qkv + t * qkv_row_stride, Q | K | V heads */
     const uint16_t *qkv;
     int64_t qkv_row_stride;
@@ -344,18 +356,18 @@ static void store_kv(const oracle_nra_args *a, void *cache, int64_t page_stride,
 static void nra_token(const oracle_nra_args *a, int64_t t, int64_t b, int64_t j, int64_t pos,
                       int64_t page, int64_t row)
 {
-    int D = a->D, Hq = a->Hq, Hkv = a->Hkv;
+    int D = a->D, Hq = a->Hq, Hkv = a->Hkv, Rr = a->rot;
     double *x = malloc(sizeof(double) * (size_t)D);
     double *y = malloc(sizeof(double) * (size_t)D);
     double *o = malloc(sizeof(double) * (size_t)D);
-    double *c = malloc(sizeof(double) * (size_t)D / 2);
-    double *s = malloc(sizeof(double) * (size_t)D / 2);
+    double *c = malloc(sizeof(double) * (size_t)(D / 2 + 1));
+    double *s = malloc(sizeof(double) * (size_t)(D / 2 + 1));
     float *v32 = malloc(sizeof(float) * (size_t)D);
     uint16_t *raw = malloc(sizeof(uint16_t) * (size_t)D);
-    /* the fp32 table values, not recomputed angles */
-    for (int i = 0; i < D / 2; ++i) {
-        c[i] = (double)a->cos_sin[pos * D + i];
-        s[i] = (double)a->cos_sin[pos * D + D / 2 + i];
+    /* the fp32 table values, not recomputed angles; table rows hold R floats */
+    for (int i = 0; i < Rr / 2; ++i) {
+        c[i] = (double)a->cos_sin[pos * Rr + i];
+        s[i] = (double)a->cos_sin[pos * Rr + Rr / 2 + i];
     }
     const uint16_t *rowp = a->qkv + t * a->qkv_row_stride;
     /* read every head of the token before any write: q_out / k_out may
@@ -368,7 +380,7 @@ static void nra_token(const oracle_nra_args *a, int64_t t, int64_t b, int64_t j,
         const uint16_t *src = tok + (int64_t)h * D;
         for (int d = 0; d < D; ++d) x[d] = oracle_bf16_to_f64(src[d]);
         oracle_rmsnorm(x, D, is_q ? a->q_w : a->k_w, a->norm, (double)a->eps, y);
-        oracle_rope(y, D, a->rope, c, s, o);
+        oracle_rope_partial(y, D, Rr, a->rope, c, s, o);
         for (int d = 0; d < D; ++d) v32[d] = (float)o[d];
         if (is_q) {
             store_q(a, t, h, b, j, v32);
@@ -391,9 +403,18 @@ static void nra_token(const oracle_nra_args *a, int64_t t, int64_t b, int64_t j,
     free(tok); free(x); free(y); free(o); free(c); free(s); free(v32); free(raw);
 }
 
+/* Whether token t is suppressed: its position lies outside the cos/sin
+ * table.  Without rotated dims (R = 0) positions are not used at all. */
+static int position_out_of_table(const oracle_nra_args *a, int64_t t)
+{
+    if (a->rot == 0) return 0;
+    int64_t pos = a->positions[t];
+    return pos < 0 || pos >= a->cs_rows;
+}
+
 int oracle_norm_rope_append(const oracle_nra_args *a)
 {
-    if (a->D % 2) return ORC_BAD_ARGS;
+    if (a->D % 2 || a->rot % 2 || a->rot < 0 || a->rot > a->D) return ORC_BAD_ARGS;
     if (a->addressing == 0) {
         int bad = nra_invalid(a);
         if (a->flags)
@@ -404,8 +425,8 @@ int oracle_norm_rope_append(const oracle_nra_args *a)
             int64_t qlen = end - beg, sl = a->seq_lens[b];
             for (int64_t j = 0; j < qlen; ++j) {
                 int64_t t = beg + j;
-                int64_t pos = a->positions[t];
-                if (pos < 0 || pos >= a->cs_rows) continue;
+                if (position_out_of_table(a, t)) continue;
+                int64_t pos = a->rot ? a->positions[t] : 0;
                 int64_t L = sl - qlen + j;            /* logical row in the request */
                 int64_t page = a->page_table[(int64_t)b * a->maxp + L / a->page_size];
                 nra_token(a, t, b, j, pos, page, L % a->page_size);
@@ -431,8 +452,8 @@ int oracle_norm_rope_append(const oracle_nra_args *a)
     /* slot addressing (vLLM reshape_and_cache): slot s -> page s / ps, row s % ps */
     int64_t capacity = (int64_t)a->num_pages * a->page_size;
     for (int64_t t = 0; t < a->T; ++t) {
-        int64_t pos = a->positions[t];
-        if (pos < 0 || pos >= a->cs_rows) continue;
+        if (position_out_of_table(a, t)) continue;
+        int64_t pos = a->rot ? a->positions[t] : 0;
         int64_t slot = a->slot_mapping[t];
         int64_t page = -1, row = 0;
         if (slot >= 0 && slot < capacity) {

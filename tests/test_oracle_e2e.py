@@ -285,6 +285,65 @@ def test_one_hot_head_reads_cos_then_sin_half_of_the_table_row():
         assert got[i + inp.D // 2] == W.bf16_round(np.array([s]))[0]
 
 
+@pytest.mark.parametrize("R", [64, 32])
+def test_partial_rotary_passes_the_nope_dims_through(R):
+    """rotary_dim R < D: with no norm and bf16 outputs, dims [R, D) of every
+    Q and K head are the input bits and dims [0, R) are the RoPE of the
+    R-dim prefix with the table row of R floats."""
+    inp = _small(q_mode=W.Q_BF16, norm=W.NORM_NONE, rotary_dim=R, kv_fp8=False)
+    assert inp.cos_sin.shape[1] == R
+    out = run_oracle(inp)
+    Hq, D = inp.Hq, inp.D
+    for t in range(inp.T):
+        pos = inp.positions[t]
+        c, s = inp.cos_sin[pos, :R // 2], inp.cos_sin[pos, R // 2:]
+        for h in range(Hq):
+            src = inp.qkv[t, h * D:(h + 1) * D]
+            got = out["q_out"][t, h]
+            assert np.array_equal(got[R:], src[R:])
+            x = W.bf16_bits_to_f32(src).astype(np.float64)
+            o = oracle.rope(x[:R], inp.rope, c, s)
+            assert np.array_equal(got[:R], W.to_bf16_bits(o.astype(np.float32)))
+
+
+def test_no_rotary_dims_copy_q_and_k_and_ignore_positions():
+    """rotary_dim 0 (a NoPE layer): no norm + bf16 makes Q and the K cache
+    rows bit copies of the input, and positions outside any table suppress
+    nothing."""
+    inp = _small(q_mode=W.Q_BF16, norm=W.NORM_NONE, rotary_dim=0, kv_fp8=False)
+    inp.positions = np.full(inp.T, -7, np.int64)
+    out = run_oracle(inp)
+    Hq, Hkv, D = inp.Hq, inp.Hkv, inp.D
+    assert np.array_equal(out["q_out"].reshape(inp.T, -1), inp.qkv[:, :Hq * D])
+    kv_changed = ~np.all(out["k_cache"] == inp.k_cache0, axis=(2, 3))
+    assert kv_changed.sum() > 0
+    t = 0
+    for b in range(inp.B):
+        ql = int(inp.q_indptr[b + 1] - inp.q_indptr[b])
+        for j in range(ql):
+            L = int(inp.seq_lens[b]) - ql + j
+            page = inp.page_table[b, L // inp.page_size]
+            assert np.array_equal(out["k_cache"][page, L % inp.page_size].reshape(-1),
+                                  inp.qkv[t, Hq * D:(Hq + Hkv) * D])
+            t += 1
+
+
+def test_head_dim_64_matches_per_head_composition():
+    """D = 64 heads (the GPT-OSS row of the vLLM issue's model table): each
+    Q head equals rmsnorm -> rope -> bf16 of the pinned step functions."""
+    inp = _small(D=64, Hq=4, Hkv=2, q_mode=W.Q_BF16, norm=W.NORM_RMS)
+    out = run_oracle(inp)
+    D = 64
+    for t in range(inp.T):
+        pos = inp.positions[t]
+        c, s = inp.cos_sin[pos, :D // 2], inp.cos_sin[pos, D // 2:]
+        for h in range(inp.Hq):
+            x = W.bf16_bits_to_f32(inp.qkv[t, h * D:(h + 1) * D]).astype(np.float64)
+            y = oracle.rmsnorm(x, inp.q_norm_weight, W.NORM_RMS, inp.eps)
+            o = oracle.rope(y, inp.rope, c, s)
+            assert np.array_equal(out["q_out"][t, h], W.to_bf16_bits(o.astype(np.float32)))
+
+
 def test_in_place_q_and_k_leave_v_and_padding_untouched():
     inp = _small(row_pad=64, q_in_place=True, k_in_place=True, norm=W.NORM_GEMMA)
     out = run_oracle(inp)

@@ -254,6 +254,48 @@ def test_rope_one_hot_and_interleaved_is_permuted_neox():
     assert np.array_equal(inter, back)
 
 
+@pytest.mark.parametrize("style", [0, 1])
+@pytest.mark.parametrize("D,R", [(128, 64), (128, 32), (128, 96), (256, 128), (64, 64), (64, 16), (128, 0)])
+def test_partial_rope_rotates_the_first_R_dims_only(style, D, R):
+    """Partial rotary (vLLM issue, model table: RoPE on part of the head,
+    NoPE on the rest): the first R dims are paired with half R/2 (NeoX) or
+    as (2i, 2i+1) and multiplied by exp(i angle) as complex numbers; the
+    remaining D - R dims are returned bit for bit."""
+    rng = np.random.default_rng(100 + D + R + style)
+    y = rng.standard_normal(D)
+    half = R // 2
+    ang = _angles(R, 1e4, 987.0) if R else np.zeros(0)
+    o = oracle.rope(y, style, np.cos(ang), np.sin(ang), rot=R)
+    assert np.array_equal(o[R:], y[R:])
+    if R:
+        if style == 0:
+            ia, ib = np.arange(half), np.arange(half) + half
+        else:
+            ia, ib = 2 * np.arange(half), 2 * np.arange(half) + 1
+        z = (y[ia] + 1j * y[ib]) * np.exp(1j * ang)
+        assert np.allclose(o[ia], z.real, rtol=0, atol=1e-14)
+        assert np.allclose(o[ib], z.imag, rtol=0, atol=1e-14)
+
+
+def test_partial_rope_one_hot_pairs_use_half_of_R():
+    # with D = 128 and R = 64, dim i < 32 pairs with i + 32 (not i + 64)
+    D, R = 128, 64
+    ang = _angles(R, 1e6, 77.0)
+    c, s = np.cos(ang), np.sin(ang)
+    for i in [0, 7, 31]:
+        e = np.zeros(D)
+        e[i] = 1.0
+        o = oracle.rope(e, 0, c, s, rot=R)
+        expect = np.zeros(D)
+        expect[i], expect[i + R // 2] = c[i], s[i]
+        assert np.array_equal(o, expect)
+    for d in [64, 100, 127]:
+        e = np.zeros(D)
+        e[d] = 1.0
+        assert np.array_equal(oracle.rope(e, 0, c, s, rot=R), e)
+        assert np.array_equal(oracle.rope(e, 1, c, s, rot=R), e)
+
+
 # ----------------------------------------------------------------------------
 # dynamic Q scale
 # ----------------------------------------------------------------------------

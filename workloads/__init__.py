@@ -78,7 +78,7 @@ class NraInputs:
     q_norm_weight: np.ndarray       # fp32 [D]
     k_norm_weight: np.ndarray       # fp32 [D]
     rope: int
-    cos_sin: np.ndarray             # fp32 [rows, D]
+    cos_sin: np.ndarray             # fp32 [rows, rot]
     positions: np.ndarray           # int64 [T]
     addressing: int
     q_indptr: np.ndarray | None     # int32 [B+1]
@@ -106,10 +106,15 @@ class NraInputs:
     flags0: np.ndarray | None
     cache_seed: int = 0
     meta: dict = field(default_factory=dict)
+    rotary_dim: int | None = None   # rotated dims per head (None: the whole head)
 
     @property
     def R(self) -> int:
         return self.Hq + 2 * self.Hkv
+
+    @property
+    def rot(self) -> int:
+        return self.D if self.rotary_dim is None else self.rotary_dim
 
     @property
     def kv_elt(self) -> int:
@@ -164,7 +169,7 @@ class NraInputs:
         d = {
             "qkv_read": T * self.R * D * 2,
             "norm_weights": (2 * D * 4) if self.norm != NORM_NONE else 0,
-            "cos_sin": T * D * 4,
+            "cos_sin": T * self.rot * 4,
             "q_write": T * Hq * D * self.q_elt,
             "q_scale": T * Hq * 4 if self.q_mode == Q_FP8_DYNAMIC else 0,
             "kv_append": T * 2 * Hkv * D * self.kv_elt,
@@ -180,7 +185,7 @@ def nra_case(*, name="custom", seed, q_lens, prior_lens, Hq, Hkv, D, page_size,
              cs_rows=None, kv_fp8=False, q_mode=Q_BF16, q_scale_padded=False, max_seqlen=0,
              upper_max=448.0, q_scale_inv=1.0, k_scale=1.0, v_scale=1.0, zero_tail=True,
              q_in_place=False, k_in_place=False, addressing=ADDR_PAGED, spare_pages=None,
-             maxp=None, host_caches=True, positions=None) -> NraInputs:
+             maxp=None, host_caches=True, positions=None, rotary_dim=None) -> NraInputs:
     """Draw one norm-rope-append call.
 
     Request b appends ``q_lens[b]`` tokens after ``prior_lens[b]`` cached
@@ -216,7 +221,8 @@ def nra_case(*, name="custom", seed, q_lens, prior_lens, Hq, Hkv, D, page_size,
     positions = np.asarray(positions, dtype=np.int64)
     if cs_rows is None:
         cs_rows = int(max(int(seq_lens.max()) if B else 1, 1))
-    cos_sin = cos_sin_table(cs_rows, D, theta)
+    rot = D if rotary_dim is None else int(rotary_dim)
+    cos_sin = cos_sin_table(cs_rows, rot, theta) if rot else np.zeros((cs_rows, 0), np.float32)
     q_indptr = np.zeros(B + 1, np.int32)
     q_indptr[1:] = np.cumsum(q_lens)
     need = (seq_lens + page_size - 1) // page_size
@@ -274,6 +280,7 @@ def nra_case(*, name="custom", seed, q_lens, prior_lens, Hq, Hkv, D, page_size,
         upper_max=upper_max, k_cache0=k_cache0, v_cache0=v_cache0, q_out0=q_out0,
         q_scale0=q_scale0, flags0=flags0, cache_seed=cache_seed,
         meta={"seed": seed, "q_lens": q_lens.tolist() if B <= 64 else None},
+        rotary_dim=rot,
     )
 
 
