@@ -92,9 +92,12 @@ typedef enum { QKPREP_ADDR_PAGED = 0, QKPREP_ADDR_SLOT = 1 } qkprep_addressing;
  * j = t - q_indptr[b], q_len = q_indptr[b+1] - q_indptr[b]):
  *   x     = head row of qkv (bf16 -> fp32)
  *   y     = x * rsqrt(mean(x^2) + eps) * w      (norm RMS; w -> 1 + w for GEMMA)
- *   o     = RoPE(y) with c_i = cos_sin[pos][i], s_i = cos_sin[pos][D/2 + i]
- *           NEOX pairs (i, i + D/2), INTERLEAVED pairs (2i, 2i + 1):
- *           (a, b) -> (a c - b s, b c + a s)
+ *   o     = RoPE(y) on the first R = rotary_dim dims, with
+ *           c_i = cos_sin[pos][i], s_i = cos_sin[pos][R/2 + i];
+ *           NEOX pairs (i, i + R/2), INTERLEAVED pairs (2i, 2i + 1), i < R/2:
+ *           (a, b) -> (a c - b s, b c + a s); dims [R, D) pass through
+ *           (partial rotary, vLLM issue's model table: RoPE on part of the
+ *           head, NoPE on the rest; R = 0 is a NoPE layer)
  *   Q     -> q_out[t][h] : bf16(o), or E4M3(o / s) with s stored in q_scale,
  *            or E4M3(o * q_scale_inv)
  *   K     -> cache row  : bf16(o) or E4M3(o / k_scale); optionally bf16(o) to k_out
@@ -103,7 +106,8 @@ typedef enum { QKPREP_ADDR_PAGED = 0, QKPREP_ADDR_SLOT = 1 } qkprep_addressing;
  * row = L % ps.  Slot addressing: page = slot / ps, row = slot % ps.
  * E4M3 is OCP E4M3FN, round to nearest even, finite overflow saturates to
  * +-448.  Positions outside [0, cos_sin_rows) suppress the whole token (no
- * byte written for it).
+ * byte written for it); with rotary_dim 0 positions and the table are not
+ * read and nothing is suppressed.
  *
  * Device validation (paged addressing only), all-or-nothing: the call is
  * invalid if q_indptr[0] != 0, q_indptr[B] != T, q_indptr decreases,
@@ -121,8 +125,8 @@ typedef struct qkprep_norm_rope_append_params {
     int32_t num_tokens;            /* T >= 0 */
     int32_t num_q_heads;           /* Hq >= 1 */
     int32_t num_kv_heads;          /* Hkv >= 1, Hq % Hkv == 0 */
-    int32_t head_dim;              /* D: 128 or 256 */
-    int32_t rotary_dim;            /* must equal head_dim */
+    int32_t head_dim;              /* D: 64, 128 or 256 */
+    int32_t rotary_dim;            /* R: rotated dims, 0 <= R <= D, multiple of 16 (R = D: whole head) */
 
     const void* qkv;               /* bf16 [T][qkv_row_stride]; heads Q(Hq) | K(Hkv) | V(Hkv), 16-B aligned */
     int64_t qkv_row_stride;        /* >= (Hq + 2 Hkv) * D, multiple of 8 */
@@ -133,9 +137,10 @@ typedef struct qkprep_norm_rope_append_params {
     const float* k_norm_weight;    /* fp32 [D], 16-B aligned; required when norm != NONE */
 
     int32_t rope;                  /* qkprep_rope */
-    const float* cos_sin_cache;    /* fp32 [cos_sin_rows][rotary_dim]: cos half | sin half, 16-B aligned */
-    int64_t cos_sin_rows;          /* >= 1 */
-    const int64_t* positions;      /* int64 [T] */
+    const float* cos_sin_cache;    /* fp32 [cos_sin_rows][rotary_dim]: cos half | sin half, 16-B aligned;
+                                      not read (may be NULL) when rotary_dim == 0 */
+    int64_t cos_sin_rows;          /* >= 1 when rotary_dim > 0 */
+    const int64_t* positions;      /* int64 [T]; not read (may be NULL) when rotary_dim == 0 */
 
     int32_t addressing;            /* qkprep_addressing */
     int32_t num_requests;          /* B; paged: 0 <= B <= 4096 (and B >= 1 when T > 0); slot: ignored */

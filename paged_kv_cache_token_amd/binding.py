@@ -146,18 +146,20 @@ def norm_rope_append_params(*, qkv, num_q_heads, num_kv_heads, head_dim, cos_sin
                             k_scale=None, v_scale=None, zero_tail=1, q_out_row_stride=None, q_mode=Q_BF16,
                             q_scale=None, q_scale_layout=QSCALE_TOKEN_HEAD, max_seqlen=0, q_scale_inv=None,
                             upper_max=448.0, k_out=None, k_out_row_stride=None, flags=None,
-                            num_tokens=None, qkv_row_stride=None, num_requests=None) -> NormRopeAppendParams:
+                            num_tokens=None, qkv_row_stride=None, num_requests=None,
+                            rotary_dim=None) -> NormRopeAppendParams:
     """Fill the params struct from tensors (shapes/strides read from them when not given)."""
     p = NormRopeAppendParams()
     p.num_tokens = qkv.shape[0] if num_tokens is None else num_tokens
-    p.num_q_heads, p.num_kv_heads, p.head_dim, p.rotary_dim = num_q_heads, num_kv_heads, head_dim, head_dim
+    p.num_q_heads, p.num_kv_heads, p.head_dim = num_q_heads, num_kv_heads, head_dim
+    p.rotary_dim = head_dim if rotary_dim is None else rotary_dim
     p.qkv = _ptr(qkv)
     p.qkv_row_stride = qkv.stride(0) if qkv_row_stride is None else qkv_row_stride
     p.norm, p.eps = norm, eps
     p.q_norm_weight, p.k_norm_weight = _ptr(q_norm_weight), _ptr(k_norm_weight)
     p.rope = rope
     p.cos_sin_cache = _ptr(cos_sin_cache)
-    p.cos_sin_rows = cos_sin_cache.shape[0]
+    p.cos_sin_rows = cos_sin_cache.shape[0] if cos_sin_cache is not None else 0
     p.positions = _ptr(positions)
     p.addressing = addressing
     if addressing == ADDR_PAGED:

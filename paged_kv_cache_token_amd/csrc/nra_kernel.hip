@@ -4,15 +4,19 @@
 // NHD paged-KV append" (Contract), TensorRT-LLM PR "Fuse Qwen3.5 gated QKV
 // preprocessing" (Phase 2: Gemma norm + RoPE folded into the KV-append
 // pass, strided rows), SGLang PR "fused Q/K RMSNorm + RoPE with
-// cos_sin_cache" (fp32 table, int64 positions).
+// cos_sin_cache" (fp32 table, int64 positions), vLLM issue "ROPE +
+// KV-Cache-Write + pre-attn prepare-ops fusion" (model table: 64-dim heads,
+// RoPE on part of the head with NoPE dims passed through).
 //
 // Mapping onto CDNA4 (one launch per call, 256-thread workgroups = 4 wave64):
-//  * A head row of D bf16 elements is owned by G = D/16 lanes (8 for D=128,
-//    16 for D=256).  Lane l of the group loads two 16-byte vectors: elements
-//    [8l, 8l+8) and [D/2 + 8l, D/2 + 8l + 8).  Every NeoX pair (i, i + D/2)
-//    and every interleaved pair (2i, 2i+1) then sits in one lane's registers:
-//    RoPE needs no LDS and no lane exchange.  A wave covers 64/G head rows of
-//    one token (a "chunk").
+//  * A head row of D bf16 elements is owned by G = D/16 lanes (4 for D=64,
+//    8 for D=128, 16 for D=256).  Lane l of the group loads two 16-byte
+//    vectors: elements [8l, 8l+8) and [R/2 + 8l, R/2 + 8l + 8) when l < R/16
+//    (R rotated dims), else the 16 pass-through elements [16l, 16l+16).
+//    Every NeoX pair (i, i + R/2) and every interleaved pair (2i, 2i+1) then
+//    sits in one lane's registers: RoPE needs no lane exchange.  The common
+//    R = D case is a separate instance with compile-time offsets.  A wave
+//    covers 64/G head rows of one token (a "chunk").
 //  * The sum of squares and the FP8 amax are reduced over the G lanes of the
 //    row only (DPP within the lane group), never across rows or tokens.
 //  * Every workgroup owns a balanced, contiguous range of the (token, chunk)
@@ -131,10 +135,68 @@ struct KvType {
     typedef typename std::conditional<KVFP8, uint8_t, uint16_t>::type type;
 };
 
+// Which two 8-element pieces of a head row lane gl of its group holds.
+// With R rotated dims (R a multiple of 16), lanes gl < R/16 ("rope lanes")
+// hold [8 gl, 8 gl + 8) and [R/2 + 8 gl, R/2 + 8 gl + 8): every NeoX pair
+// (i, i + R/2) and every interleaved pair (2i, 2i+1) then sits in one
+// lane's registers.  The other lanes hold 16 pass-through dims
+// [16 gl, 16 gl + 16).  For R = D this is the split [8 gl, ..) | [D/2 + 8 gl, ..).
+struct LaneMap {
+    int o0, o1;      // element offsets of the two vectors in the head row
+    int hr, qr;      // R/2 and R/4: offsets of the sine half and of the second vector's angles
+    int fp8_store;   // 0: one 16-byte store; 1: swap a half with the neighbour lane; 2: two 8-byte stores
+    bool rope;
+};
+
+template <int D, bool PART>
+__device__ __forceinline__ LaneMap lane_map(int rot, int gl) {
+    LaneMap m;
+    if constexpr (!PART) {
+        // whole head rotates: compile-time split, immediate store offsets
+        m.rope = true;
+        m.o0 = 8 * gl;
+        m.o1 = D / 2 + 8 * gl;
+        m.hr = D / 2;
+        m.qr = D / 4;
+        m.fp8_store = 1;
+        return m;
+    }
+    m.rope = gl < (rot >> 4);
+    m.hr = rot >> 1;
+    m.qr = rot >> 2;
+    m.o0 = m.rope ? 8 * gl : 16 * gl;
+    m.o1 = m.rope ? (rot >> 1) + 8 * gl : 16 * gl + 8;
+    // rope lanes pair up (and the swapped 16 bytes stay 16-byte aligned)
+    // when R/2 is a multiple of 16
+    m.fp8_store = !m.rope ? 0 : ((rot & 31) == 0 ? 1 : 2);
+    return m;
+}
+
+// E4M3 codes of the lane's two pieces (lo at o0, hi at o1) into a head row
+// of bytes.  Paired rope lanes trade one 8-byte half so that each writes 16
+// contiguous bytes: the even lane [o0, o0 + 16), the odd lane [o1 - 8, o1 + 8).
+__device__ __forceinline__ void store_fp8_lane(uint8_t* row, int gl, const LaneMap& m, uint2 lo, uint2 hi) {
+    const bool odd = gl & 1;
+    const uint2 send = odd ? lo : hi;
+    uint2 recv;
+    recv.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.x, kDppQuadSwap1, 0xF, 0xF, false);
+    recv.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.y, kDppQuadSwap1, 0xF, 0xF, false);
+    if (m.fp8_store == 1) {
+        const uint4 v = odd ? make_uint4(recv.x, recv.y, hi.x, hi.y) : make_uint4(lo.x, lo.y, recv.x, recv.y);
+        st16(row + (odd ? m.o1 - 8 : m.o0), v);
+    } else if (m.fp8_store == 0) {
+        st16(row + m.o0, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    } else {
+        st8(row + m.o0, lo);
+        st8(row + m.o1, hi);
+    }
+}
+
 // Encodes and stores head row r of tile token ti (global token t) whose two
-// 16-byte vectors v0 / v1 are in registers.  Q/K rows: RMSNorm (weights
-// from LDS), RoPE (cos/sin row from LDS), then bf16 / E4M3.  V rows: copy
-// or E4M3.  `c` holds the per-call constants.
+// 16-byte vectors v0 / v1 (elements at lm.o0 / lm.o1) are in registers.
+// Q/K rows: RMSNorm (weights from LDS), RoPE on the rotated dims (cos/sin
+// row from LDS), then bf16 / E4M3.  V rows: copy or E4M3.  `k` holds the
+// per-call constants.
 struct RowConsts {
     float inv_k, inv_v, q_static, inv_um;
     int qs_hstride;
@@ -142,26 +204,26 @@ struct RowConsts {
 };
 
 template <int D, int QMODE, bool KVFP8>
-__device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, int r, int gl, uint4 v0, uint4 v1,
-                                            const float* s_w, const float* s_cs_row, const int64_t* s_koff,
-                                            const int64_t* s_voff, const int64_t* s_qsoff, const RowConsts& k) {
+__device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, int r, int gl, const LaneMap& lm,
+                                            uint4 v0, uint4 v1, const float* s_w, const float* s_cs_row,
+                                            const int64_t* s_koff, const int64_t* s_voff, const int64_t* s_qsoff,
+                                            const RowConsts& k) {
     constexpr int G = D / 16;
-    constexpr int HALF = D / 2;
     typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
     if (r >= a.Hq + a.Hkv) {
         // V head: raw copy (bf16 cache) or x / v_scale (FP8 cache)
         const int64_t voff = s_voff[ti];
         if (voff < 0) return;
-        kv_t* dst = reinterpret_cast<kv_t*>(a.v_cache) + voff + (r - a.Hq - a.Hkv) * D + 8 * gl;
+        kv_t* row = reinterpret_cast<kv_t*>(a.v_cache) + voff + (r - a.Hq - a.Hkv) * D;
         if constexpr (KVFP8) {
             float x[16];
             unpack8(v0, x);
             unpack8(v1, x + 8);
-            store_fp8_row(reinterpret_cast<uint8_t*>(dst) - 8 * gl, gl, HALF, pack8_fp8(x, k.inv_v),
-                          pack8_fp8(x + 8, k.inv_v));
+            store_fp8_lane(reinterpret_cast<uint8_t*>(row), gl, lm, pack8_fp8(x, k.inv_v),
+                           pack8_fp8(x + 8, k.inv_v));
         } else {
-            st16(dst, v0);
-            st16(dst + HALF, v1);
+            st16(row + lm.o0, v0);
+            st16(row + lm.o1, v1);
         }
         return;
     }
@@ -176,54 +238,58 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
         ss = group_sum<G>(ss);
         const float inv = rsqrtf(fmaf(ss, 1.0f / (float)D, a.eps));
         const float* w = s_w + (is_q ? 0 : D);
-        const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * gl);
-        const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * gl + 4);
-        const float4 w2 = *reinterpret_cast<const float4*>(w + HALF + 8 * gl);
-        const float4 w3 = *reinterpret_cast<const float4*>(w + HALF + 8 * gl + 4);
+        const float4 w0 = *reinterpret_cast<const float4*>(w + lm.o0);
+        const float4 w1 = *reinterpret_cast<const float4*>(w + lm.o0 + 4);
+        const float4 w2 = *reinterpret_cast<const float4*>(w + lm.o1);
+        const float4 w3 = *reinterpret_cast<const float4*>(w + lm.o1 + 4);
         const float wv[16] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w,
                               w2.x, w2.y, w2.z, w2.w, w3.x, w3.y, w3.z, w3.w};
 #pragma unroll
         for (int i = 0; i < 16; ++i) x[i] = x[i] * inv * wv[i];
     }
-    if (a.rope == 0) {
-        // NeoX: pair i of the lane = dims (8 gl + i, D/2 + 8 gl + i), angle 8 gl + i
-        const float4 c0 = *reinterpret_cast<const float4*>(s_cs_row + 8 * gl);
-        const float4 c1 = *reinterpret_cast<const float4*>(s_cs_row + 8 * gl + 4);
-        const float4 s0 = *reinterpret_cast<const float4*>(s_cs_row + HALF + 8 * gl);
-        const float4 s1 = *reinterpret_cast<const float4*>(s_cs_row + HALF + 8 * gl + 4);
-        const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    if (lm.rope) {
+        const int hr = lm.hr;
+        if (a.rope == 0) {
+            // NeoX: pair i of the lane = dims (8 gl + i, R/2 + 8 gl + i), angle 8 gl + i
+            const float4 c0 = *reinterpret_cast<const float4*>(s_cs_row + 8 * gl);
+            const float4 c1 = *reinterpret_cast<const float4*>(s_cs_row + 8 * gl + 4);
+            const float4 s0 = *reinterpret_cast<const float4*>(s_cs_row + hr + 8 * gl);
+            const float4 s1 = *reinterpret_cast<const float4*>(s_cs_row + hr + 8 * gl + 4);
+            const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float xa = x[i], xb = x[8 + i];
-            x[i] = xa * c[i] - xb * s[i];
-            x[8 + i] = xb * c[i] + xa * s[i];
-        }
-    } else {
-        // interleaved: the first vector holds angles 4 gl .. 4 gl + 3, the
-        // second D/4 + 4 gl .. D/4 + 4 gl + 3
-        const float4 c0 = *reinterpret_cast<const float4*>(s_cs_row + 4 * gl);
-        const float4 c1 = *reinterpret_cast<const float4*>(s_cs_row + D / 4 + 4 * gl);
-        const float4 s0 = *reinterpret_cast<const float4*>(s_cs_row + HALF + 4 * gl);
-        const float4 s1 = *reinterpret_cast<const float4*>(s_cs_row + HALF + D / 4 + 4 * gl);
-        const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            for (int i = 0; i < 8; ++i) {
+                const float xa = x[i], xb = x[8 + i];
+                x[i] = xa * c[i] - xb * s[i];
+                x[8 + i] = xb * c[i] + xa * s[i];
+            }
+        } else {
+            // interleaved: the first vector holds angles 4 gl .. 4 gl + 3, the
+            // second R/4 + 4 gl .. R/4 + 4 gl + 3
+            const int qr = lm.qr;
+            const float4 c0 = *reinterpret_cast<const float4*>(s_cs_row + 4 * gl);
+            const float4 c1 = *reinterpret_cast<const float4*>(s_cs_row + qr + 4 * gl);
+            const float4 s0 = *reinterpret_cast<const float4*>(s_cs_row + hr + 4 * gl);
+            const float4 s1 = *reinterpret_cast<const float4*>(s_cs_row + hr + qr + 4 * gl);
+            const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int i0 = (m < 4) ? 2 * m : 8 + 2 * (m - 4);
-            const float xa = x[i0], xb = x[i0 + 1];
-            x[i0] = xa * c[m] - xb * s[m];
-            x[i0 + 1] = xb * c[m] + xa * s[m];
+            for (int m = 0; m < 8; ++m) {
+                const int i0 = (m < 4) ? 2 * m : 8 + 2 * (m - 4);
+                const float xa = x[i0], xb = x[i0 + 1];
+                x[i0] = xa * c[m] - xb * s[m];
+                x[i0 + 1] = xb * c[m] + xa * s[m];
+            }
         }
     }
     if (is_q) {
         const int h = r;
         if constexpr (QMODE == 0) {
-            uint16_t* dst = reinterpret_cast<uint16_t*>(a.q_out) + (int64_t)t * a.q_out_stride + h * D + 8 * gl;
-            st16(dst, pack8_bf16(x));
-            st16(dst + HALF, pack8_bf16(x + 8));
+            uint16_t* row = reinterpret_cast<uint16_t*>(a.q_out) + (int64_t)t * a.q_out_stride + h * D;
+            st16(row + lm.o0, pack8_bf16(x));
+            st16(row + lm.o1, pack8_bf16(x + 8));
         } else {
-            uint8_t* dst = reinterpret_cast<uint8_t*>(a.q_out) + (int64_t)t * a.q_out_stride + h * D + 8 * gl;
+            uint8_t* row = reinterpret_cast<uint8_t*>(a.q_out) + (int64_t)t * a.q_out_stride + h * D;
             float mul = k.q_static;
             if constexpr (QMODE == 1) {
                 float amax = 0.0f;
@@ -238,25 +304,25 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
                     else a.q_scale[s_qsoff[ti] + (int64_t)h * k.qs_hstride] = sc;
                 }
             }
-            store_fp8_row(dst - 8 * gl, gl, HALF, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
+            store_fp8_lane(row, gl, lm, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
         }
     } else {
         const int kh = r - a.Hq;
         const int64_t koff = s_koff[ti];
         if (koff >= 0) {
-            kv_t* dst = reinterpret_cast<kv_t*>(a.k_cache) + koff + kh * D + 8 * gl;
+            kv_t* row = reinterpret_cast<kv_t*>(a.k_cache) + koff + kh * D;
             if constexpr (KVFP8) {
-                store_fp8_row(reinterpret_cast<uint8_t*>(dst) - 8 * gl, gl, HALF, pack8_fp8(x, k.inv_k),
-                              pack8_fp8(x + 8, k.inv_k));
+                store_fp8_lane(reinterpret_cast<uint8_t*>(row), gl, lm, pack8_fp8(x, k.inv_k),
+                               pack8_fp8(x + 8, k.inv_k));
             } else {
-                st16(dst, pack8_bf16(x));
-                st16(dst + HALF, pack8_bf16(x + 8));
+                st16(row + lm.o0, pack8_bf16(x));
+                st16(row + lm.o1, pack8_bf16(x + 8));
             }
         }
         if (a.k_out) {
-            uint16_t* ko = a.k_out + (int64_t)t * a.k_out_stride + kh * D + 8 * gl;
-            st16(ko, pack8_bf16(x));
-            st16(ko + HALF, pack8_bf16(x + 8));
+            uint16_t* ko = a.k_out + (int64_t)t * a.k_out_stride + kh * D;
+            st16(ko + lm.o0, pack8_bf16(x));
+            st16(ko + lm.o1, pack8_bf16(x + 8));
         }
     }
 }
@@ -273,11 +339,10 @@ struct Cursor {
     }
 };
 
-template <int D, int QMODE, bool KVFP8>
+template <int D, int QMODE, bool KVFP8, bool PART>
 __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) {
     constexpr int G = D / 16;        // lanes per head row
     constexpr int RPW = 64 / G;      // head rows per wave
-    constexpr int HALF = D / 2;
     constexpr int U = kBatch;
     constexpr int D4 = D / 4;        // float4 per cos/sin row
     typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
@@ -300,6 +365,7 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     const int wave = tid >> 6;
     const int grp = lane / G;        // head-row slot of this lane in the wave
     const int gl = lane % G;         // lane inside the head row
+    const LaneMap lm = lane_map<D, PART>(a.rot, gl);
     int* s_indptr = s_dyn;
     int* s_seqlen = s_dyn + (a.B + 1);
     int* s_pre = s_dyn + (2 * a.B + 1);
@@ -340,9 +406,9 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
             const bool ok = ld.left > 0 && r < a.R;
             const int rr = ok ? r : 0;
             const int tt = ld.left > 0 ? ld.t : t_first;
-            const uint16_t* src = a.qkv + (int64_t)tt * a.qkv_stride + rr * D + 8 * gl;
-            buf[u][0] = ld16(src);
-            buf[u][1] = ld16(src + HALF);
+            const uint16_t* src = a.qkv + (int64_t)tt * a.qkv_stride + rr * D;
+            buf[u][0] = ld16(src + lm.o0);
+            buf[u][1] = ld16(src + lm.o1);
             ld.advance(CPT);
         }
     };
@@ -363,8 +429,9 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     auto stage_positions = [&]() {
         if (tid < ntok) {
             const int t = t_first + tid;
-            const int64_t p64 = a.positions[t];
-            s_pos[tid] = (p64 >= 0 && p64 < a.cs_rows) ? (int)p64 : -1;
+            // without rotated dims positions are not read and never suppress
+            const int64_t p64 = a.rot > 0 ? a.positions[t] : 0;
+            s_pos[tid] = (a.rot == 0 || (p64 >= 0 && p64 < a.cs_rows)) ? (int)p64 : -1;
             if (!a.paged) {
                 int64_t koff = -1, voff = -1;
                 const int64_t slot = a.slot_mapping[t];
@@ -397,11 +464,13 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
             s_voff[tid] = page * a.v_page_stride + row * row_elems;
             s_qsoff[tid] = a.q_scale_padded ? (int64_t)b * a.Hq * a.q_scale_P + j : (int64_t)t * a.Hq;
         }
+        // table rows hold R floats (staged at a stride of D)
         for (int k = tid; k < ntok * D4; k += kBlockThreads) {
             const int i = k / D4;
             const int c4 = k - i * D4;
             const int p = s_pos[i];
-            if (p >= 0) *reinterpret_cast<float4*>(s_cs + i * D + 4 * c4) = ldf4(a.cos_sin + (int64_t)p * D + 4 * c4);
+            if (p >= 0 && 4 * c4 < a.rot)
+                *reinterpret_cast<float4*>(s_cs + i * D + 4 * c4) = ldf4(a.cos_sin + (int64_t)p * a.rot + 4 * c4);
         }
     };
 
@@ -474,8 +543,8 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
                 const int r = pr.c * RPW + grp;
                 const int ti = pr.t - t_first;
                 if (r < a.R && s_pos[ti] >= 0)
-                    process_row<D, QMODE, KVFP8>(a, pr.t, ti, r, gl, buf[u][0], buf[u][1], s_w, s_cs + ti * D,
-                                                 s_koff, s_voff, s_qsoff, kc);
+                    process_row<D, QMODE, KVFP8>(a, pr.t, ti, r, gl, lm, buf[u][0], buf[u][1], s_w,
+                                                 s_cs + ti * D, s_koff, s_voff, s_qsoff, kc);
                 pr.advance(CPT);
             }
         }
@@ -552,7 +621,7 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
 }
 
 // workgroups per CU the kernel can keep resident (queried once per device)
-template <int D, int QMODE, bool KVFP8>
+template <int D, int QMODE, bool KVFP8, bool PART>
 int resident_blocks(size_t lds) {
     static int cached_dev = -1, cached = 0, cached_cus = 0;
     static size_t cached_lds = (size_t)-1;
@@ -560,7 +629,7 @@ int resident_blocks(size_t lds) {
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (dev != cached_dev || lds != cached_lds) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nra_kernel<D, QMODE, KVFP8>, kBlockThreads,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nra_kernel<D, QMODE, KVFP8, PART>, kBlockThreads,
                                                          lds) != hipSuccess)
             per_cu = 1;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
@@ -573,13 +642,13 @@ int resident_blocks(size_t lds) {
     return cached;
 }
 
-template <int D, int QMODE, bool KVFP8>
+template <int D, int QMODE, bool KVFP8, bool PART>
 hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     size_t lds = a.paged ? (size_t)(3 * a.B + 2) * sizeof(int) : 0;
     if (a.stage_q_scale) lds = (size_t)((3 * a.B + 2 + 3) & ~3) * sizeof(int) + (size_t)kMaxTokensPerTile * a.Hq * sizeof(float);
     // enough workgroups to fill every CU, none with less than 8 head-row
     // chunks of work, and at least one per 4 requests for the tail clears
-    const int64_t cap = resident_blocks<D, QMODE, KVFP8>(lds);
+    const int64_t cap = resident_blocks<D, QMODE, KVFP8, PART>(lds);
     int64_t want = (a.total_items + 7) / 8;
     if (want < (a.B + 3) / 4) want = (a.B + 3) / 4;
     if (want < 1) want = 1;
@@ -591,7 +660,7 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     // HBM accesses of the moment close together (about 6 % faster on a
     // 15k-token prefill).  Short calls keep one contiguous range each.
     la.interleave = (a.T >= 8 * (int64_t)la.grid) ? 4 * a.chunks_per_token : 0;
-    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
+    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, PART>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();
 }
 
@@ -600,7 +669,11 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
 hipError_t launch_norm_rope_append(const NraDevArgs& a, int head_dim, int q_mode, int kv_fp8,
                                    hipStream_t stream) {
 #define QKPREP_NRA_CASE(DD, QM, KF) \
-    if (head_dim == DD && q_mode == QM && (kv_fp8 != 0) == KF) return launch_t<DD, QM, KF>(a, stream);
+    if (head_dim == DD && q_mode == QM && (kv_fp8 != 0) == KF)                                         \
+        return a.rot == DD ? launch_t<DD, QM, KF, false>(a, stream) : launch_t<DD, QM, KF, true>(a, stream);
+    QKPREP_NRA_CASE(64, 0, false) QKPREP_NRA_CASE(64, 0, true)
+    QKPREP_NRA_CASE(64, 1, false) QKPREP_NRA_CASE(64, 1, true)
+    QKPREP_NRA_CASE(64, 2, false) QKPREP_NRA_CASE(64, 2, true)
     QKPREP_NRA_CASE(128, 0, false) QKPREP_NRA_CASE(128, 0, true)
     QKPREP_NRA_CASE(128, 1, false) QKPREP_NRA_CASE(128, 1, true)
     QKPREP_NRA_CASE(128, 2, false) QKPREP_NRA_CASE(128, 2, true)

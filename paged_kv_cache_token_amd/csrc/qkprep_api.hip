@@ -42,8 +42,9 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     if (p->struct_size != sizeof(qkprep_norm_rope_append_params)) return QKPREP_E_VERSION;
     const int T = p->num_tokens, Hq = p->num_q_heads, Hkv = p->num_kv_heads, D = p->head_dim;
     if (T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return QKPREP_E_SHAPE;
-    if (D != 128 && D != 256) return QKPREP_E_UNSUPPORTED;
-    if (p->rotary_dim != D) return QKPREP_E_UNSUPPORTED;
+    if (D != 64 && D != 128 && D != 256) return QKPREP_E_UNSUPPORTED;
+    const int rot = p->rotary_dim;
+    if (rot < 0 || rot > D || rot % 16) return QKPREP_E_UNSUPPORTED;
     if (p->norm < 0 || p->norm > 2 || p->rope < 0 || p->rope > 1 || p->addressing < 0 ||
         p->addressing > 1 || p->kv_dtype < 0 || p->kv_dtype > 1 || p->q_mode < 0 || p->q_mode > 2 ||
         p->q_scale_layout < 0 || p->q_scale_layout > 1)
@@ -74,7 +75,8 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     if (p->kv_dtype == QKPREP_FP8_E4M3 && (!p->k_scale || !p->v_scale)) return QKPREP_E_NULL;
     if (paged && (!p->q_indptr || !p->seq_lens || !p->page_table || !p->flags)) return QKPREP_E_NULL;
     if (T > 0) {
-        if (!p->qkv || !p->cos_sin_cache || !p->positions || !p->q_out) return QKPREP_E_NULL;
+        if (!p->qkv || !p->q_out) return QKPREP_E_NULL;
+        if (rot > 0 && (!p->cos_sin_cache || !p->positions)) return QKPREP_E_NULL;
         if (p->norm != 0 && (!p->q_norm_weight || !p->k_norm_weight)) return QKPREP_E_NULL;
         if (!paged && !p->slot_mapping) return QKPREP_E_NULL;
         if (p->q_mode == QKPREP_Q_FP8_DYNAMIC && !p->q_scale) return QKPREP_E_NULL;
@@ -94,8 +96,9 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
         if (p->qkv_row_stride % 8) return QKPREP_E_ALIGN;
         if (p->q_out_row_stride < (int64_t)Hq * D) return QKPREP_E_SHAPE;
         if ((p->q_out_row_stride * q_elt) % 16) return QKPREP_E_ALIGN;
-        if (p->cos_sin_rows < 1) return QKPREP_E_SHAPE;
-        if (!aligned16(p->qkv) || !aligned16(p->q_out) || !aligned16(p->cos_sin_cache)) return QKPREP_E_ALIGN;
+        if (rot > 0 && p->cos_sin_rows < 1) return QKPREP_E_SHAPE;
+        if (!aligned16(p->qkv) || !aligned16(p->q_out)) return QKPREP_E_ALIGN;
+        if (rot > 0 && !aligned16(p->cos_sin_cache)) return QKPREP_E_ALIGN;
         if (p->norm != 0 && (!aligned16(p->q_norm_weight) || !aligned16(p->k_norm_weight)))
             return QKPREP_E_ALIGN;
         if (p->k_out) {
@@ -111,8 +114,10 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     a.norm = p->norm; a.eps = p->eps;
     a.q_w = p->q_norm_weight; a.k_w = p->k_norm_weight;
     a.rope = p->rope;
-    a.cos_sin = p->cos_sin_cache; a.cs_rows = p->cos_sin_rows;
-    a.positions = p->positions;
+    a.rot = rot;
+    a.cos_sin = rot > 0 ? p->cos_sin_cache : nullptr;
+    a.cs_rows = rot > 0 ? p->cos_sin_rows : 0;
+    a.positions = rot > 0 ? p->positions : nullptr;
     a.paged = paged ? 1 : 0;
     a.B = B;
     a.q_indptr = p->q_indptr; a.seq_lens = p->seq_lens; a.page_table = p->page_table;

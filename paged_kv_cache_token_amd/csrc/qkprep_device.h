@@ -128,20 +128,20 @@ __device__ __forceinline__ float dpp_f(float v) {
 // group receives the total.  All lanes of the group must be active.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-    static_assert(G == 8 || G == 16, "lane groups of 8 or 16");
+    static_assert(G == 4 || G == 8 || G == 16, "lane groups of 4, 8 or 16");
     v += dpp_f<kDppQuadSwap1>(v);
     v += dpp_f<kDppQuadSwap2>(v);
-    v += dpp_f<kDppRowHalfMirror>(v);      // lane i <- lane 7 - i (other quad of the 8)
-    if constexpr (G == 16) v += dpp_f<kDppRowMirror>(v);  // lane i <- lane 15 - i
+    if constexpr (G >= 8) v += dpp_f<kDppRowHalfMirror>(v);  // lane i <- lane 7 - i (other quad of the 8)
+    if constexpr (G == 16) v += dpp_f<kDppRowMirror>(v);     // lane i <- lane 15 - i
     return v;
 }
 
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
-    static_assert(G == 8 || G == 16, "lane groups of 8 or 16");
+    static_assert(G == 4 || G == 8 || G == 16, "lane groups of 4, 8 or 16");
     v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap1>(v));
     v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap2>(v));
-    v = __builtin_fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+    if constexpr (G >= 8) v = __builtin_fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
     if constexpr (G == 16) v = __builtin_fmaxf(v, dpp_f<kDppRowMirror>(v));
     return v;
 }

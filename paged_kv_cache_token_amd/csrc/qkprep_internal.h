@@ -30,7 +30,8 @@ struct NraDevArgs {
     const float* q_w;
     const float* k_w;
     int32_t rope;                       // 0 neox, 1 interleaved
-    const float* cos_sin;
+    int32_t rot;                        // rotated dims per head: 0..D, multiple of 16
+    const float* cos_sin;               // [cs_rows, rot]
     int64_t cs_rows;
     const int64_t* positions;
     int32_t paged;                      // 1 page table, 0 slot mapping

@@ -131,7 +131,7 @@ class DeviceNra:
             q_scale_layout=qp.QSCALE_REQ_HEAD_PADDED if inp.q_scale_padded else qp.QSCALE_TOKEN_HEAD,
             max_seqlen=inp.max_seqlen, q_scale_inv=self.q_scale_inv, upper_max=inp.upper_max,
             k_out=k_out, k_out_row_stride=inp.qkv_row_stride,
-            flags=None if self.flags is None else self.flags.t,
+            flags=None if self.flags is None else self.flags.t, rotary_dim=inp.rot,
         )
 
     def run(self, stream=None):
@@ -255,7 +255,7 @@ def written_cells(inp: W.NraInputs, pages_index=None):
     rows = inp.cos_sin.shape[0]
     for t in range(inp.T):
         pos = int(inp.positions[t])
-        if pos < 0 or pos >= rows:
+        if inp.rot > 0 and (pos < 0 or pos >= rows):
             continue
         if inp.addressing == W.ADDR_PAGED:
             b = int(np.searchsorted(inp.q_indptr, t, side="right") - 1)
@@ -280,7 +280,8 @@ def compare_nra(inp: W.NraInputs, gpu: dict, ref: dict) -> dict:
         check_exact(gpu["flags"], ref["flags"], "flags")
     invalid = ref["flags"] is not None and ref["flags"].size and (ref["flags"] == -1).all()
     rows = inp.cos_sin.shape[0]
-    live = np.array([0 <= int(p) < rows for p in inp.positions], bool) if inp.T else np.zeros(0, bool)
+    live = np.array([inp.rot == 0 or 0 <= int(p) < rows for p in inp.positions], bool) if inp.T \
+        else np.zeros(0, bool)
     if invalid:
         live[:] = False
     # caches: token rows with tolerance, every other byte exact

@@ -75,8 +75,13 @@ def _status(p):
 
 
 @pytest.mark.parametrize("over,expect", [
-    (dict(head_dim=64, rotary_dim=64), 3),
-    (dict(rotary_dim=64), 3),
+    (dict(head_dim=96, rotary_dim=96), 3),
+    (dict(head_dim=512, rotary_dim=512), 3),
+    (dict(rotary_dim=72), 3),
+    (dict(rotary_dim=144), 3),
+    (dict(rotary_dim=-16), 3),
+    (dict(cos_sin_cache=None), 1),
+    (dict(positions=None), 1),
     (dict(num_kv_heads=3), 2),
     (dict(page_size=0), 5),
     (dict(page_size=-16), 5),

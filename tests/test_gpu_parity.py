@@ -99,7 +99,7 @@ def _ragged(seed, B=6, max_q=40, max_prior=300):
     return q, prior
 
 
-@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("norm", [W.NORM_NONE, W.NORM_RMS, W.NORM_GEMMA])
 @pytest.mark.parametrize("q_mode", [W.Q_BF16, W.Q_FP8_DYNAMIC, W.Q_FP8_STATIC])
 @pytest.mark.parametrize("kv_fp8", [False, True])
@@ -118,6 +118,36 @@ def test_heads_pages_rope(rope, heads, ps):
     q, prior = _ragged(heads[0] + ps + rope, B=5, max_q=20, max_prior=200)
     inp = W.nra_case(seed=7 + ps, q_lens=q, prior_lens=prior, Hq=heads[0], Hkv=heads[1], D=128, page_size=ps,
                      rope=rope, q_mode=W.Q_FP8_DYNAMIC, kv_fp8=True, k_scale=0.05, v_scale=0.05)
+    run_and_compare(inp)
+
+
+# rotated dims R < D: R/16 rope lanes per head row, the rest pass through;
+# R/2 a multiple of 16 pairs the rope lanes for 16-byte FP8 stores, other R
+# store 8-byte halves; R = 0 reads no positions
+@pytest.mark.parametrize("D,R", [(128, 64), (128, 32), (128, 96), (128, 48), (128, 16), (128, 0),
+                                 (256, 128), (256, 80), (256, 64), (64, 32), (64, 16), (64, 48), (64, 0)])
+@pytest.mark.parametrize("arm", ["fp8", "bf16"])
+def test_partial_rotary(D, R, arm):
+    q, prior = _ragged(D + R, B=5, max_q=30, max_prior=200)
+    fp8 = arm == "fp8"
+    inp = W.nra_case(seed=D * 7 + R, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=D, page_size=16,
+                     rotary_dim=R, rope=W.ROPE_NEOX if fp8 else W.ROPE_INTERLEAVED,
+                     norm=W.NORM_RMS if fp8 else W.NORM_GEMMA,
+                     q_mode=W.Q_FP8_DYNAMIC if fp8 else W.Q_BF16, kv_fp8=fp8, k_scale=0.05, v_scale=0.05,
+                     k_in_place=not fp8, q_in_place=not fp8, row_pad=0 if fp8 else 64)
+    if R == 0:
+        inp.positions = inp.positions.copy()
+        inp.positions[:3] = -9          # not read without rotated dims
+    run_and_compare(inp)
+
+
+def test_head_dim_64_gqa_8_to_1():
+    """64 Q heads over 8 KV heads of 64 dims (the GPT-OSS row of the vLLM
+    issue's model table), FP8 Q with padded scales and E4M3 caches."""
+    q, prior = _ragged(64, B=6, max_q=70, max_prior=500)
+    inp = W.nra_case(seed=64, q_lens=q, prior_lens=prior, Hq=64, Hkv=8, D=64, page_size=16,
+                     q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=True, max_seqlen=128, kv_fp8=True,
+                     k_scale=0.05, v_scale=0.05)
     run_and_compare(inp)
 
 
