@@ -179,6 +179,9 @@ class _MlaArgs(ctypes.Structure):
         ("positions", ctypes.c_void_p), ("slot_mapping", ctypes.c_void_p),
         ("kv_cache", ctypes.c_void_p), ("kv_fp8", ctypes.c_int32), ("num_blocks", ctypes.c_int64),
         ("block_size", ctypes.c_int32), ("block_stride", ctypes.c_int64), ("kv_scale", ctypes.c_float),
+        ("q_mode", ctypes.c_int32), ("q_out", ctypes.c_void_p), ("q_out_token_stride", ctypes.c_int64),
+        ("q_out_head_stride", ctypes.c_int64), ("q_scale", ctypes.c_void_p), ("q_scale_inv", ctypes.c_float),
+        ("upper_max", ctypes.c_float),
     ]
 
 
@@ -268,7 +271,9 @@ def norm_rope_append(inp, out) -> NraResult:
 
 
 def mla_concat_rope_append(inp, out) -> None:
-    """Run the MLA oracle; ``out`` holds ``q`` (updated in place) and ``kv_cache``."""
+    """Run the MLA oracle; ``out`` holds ``q`` (updated in place in the bf16
+    Q mode), ``kv_cache`` and, in the FP8 Q modes, ``q_out`` (and ``q_scale``
+    for the dynamic one)."""
     q = _need(out["q"], np.uint16)
     cache = _need(out["kv_cache"], np.uint8 if inp.kv_fp8 else np.uint16)
     a = _MlaArgs()
@@ -291,6 +296,16 @@ def mla_concat_rope_append(inp, out) -> None:
     a.block_size = inp.block_size
     a.block_stride = inp.block_size * (inp.kv_lora_rank + inp.rope_dim)
     a.kv_scale = inp.kv_scale
+    a.q_mode = inp.q_mode
+    if inp.q_mode != 0:
+        q_out = _need(out["q_out"], np.uint8)
+        a.q_out = _ptr(q_out)
+        a.q_out_token_stride = inp.H * (inp.nope_dim + inp.rope_dim)
+        a.q_out_head_stride = inp.nope_dim + inp.rope_dim
+        a.q_scale_inv = inp.q_scale_inv
+        a.upper_max = inp.upper_max
+        if inp.q_mode == 1:
+            a.q_scale = _ptr(_need(out["q_scale"], np.float32))
     rc = lib().oracle_mla_concat_rope_append(ctypes.byref(a))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")

@@ -488,7 +488,52 @@ typedef struct {
     int32_t block_size;
     int64_t block_stride;             /* elements */
     float kv_scale;
+    /* Q output: 0 = RoPE in place in q (bf16); 1 = E4M3 with one dynamic
+     * scale per token over all its heads; 2 = E4M3 with a static scale */
+    int32_t q_mode;
+    uint8_t *q_out;                   /* E4M3 codes, [T, H, nope + rope] via strides */
+    int64_t q_out_token_stride, q_out_head_stride;
+    float *q_scale;                   /* [T], q_mode 1 */
+    float q_scale_inv;                /* q_mode 2 */
+    float upper_max;                  /* q_mode 1 */
 } oracle_mla_args;
+
+/* Q of one token in the FP8 modes (vLLM issue: the FlashInfer MLA RoPE +
+ * quantize kernel, and the question of static per-tensor and dynamic
+ * per-token scales).  Every head's [q_nope | RoPE(q_rope)] is rounded once
+ * to fp32 (v32; q_nope is exact), then encoded E4M3(v32 * q_scale_inv)
+ * (static) or E4M3(v32 / s) with s = max(amax, 1e-6) / upper_max over all
+ * heads and dims of the token (dynamic), s stored at q_scale[t].  q itself
+ * is not modified. */
+static void mla_q_fp8(const oracle_mla_args *a, int64_t t, const double *c, const double *s)
+{
+    int N = a->nope_dim, R = a->rope_dim, W = N + R;
+    float *v32 = malloc(sizeof(float) * (size_t)a->H * (size_t)W);
+    double *x = malloc(sizeof(double) * (size_t)R);
+    double *o = malloc(sizeof(double) * (size_t)R);
+    for (int h = 0; h < a->H; ++h) {
+        const uint16_t *qh = a->q + t * a->q_token_stride + (int64_t)h * a->q_head_stride;
+        float *vh = v32 + (int64_t)h * W;
+        for (int d = 0; d < N; ++d) vh[d] = (float)oracle_bf16_to_f64(qh[d]);
+        for (int d = 0; d < R; ++d) x[d] = oracle_bf16_to_f64(qh[N + d]);
+        oracle_rope(x, R, a->rope, c, s, o);
+        for (int d = 0; d < R; ++d) vh[N + d] = (float)o[d];
+    }
+    double sc = 0.0;
+    if (a->q_mode == 1) {
+        float st = oracle_q_scale(v32, a->H * W, (double)a->upper_max);
+        a->q_scale[t] = st;
+        sc = (double)st;
+    }
+    for (int h = 0; h < a->H; ++h) {
+        uint8_t *dst = a->q_out + t * a->q_out_token_stride + (int64_t)h * a->q_out_head_stride;
+        const float *vh = v32 + (int64_t)h * W;
+        for (int d = 0; d < W; ++d)
+            dst[d] = (a->q_mode == 1) ? oracle_f64_to_e4m3((double)vh[d] / sc)
+                                      : oracle_f64_to_e4m3((double)vh[d] * (double)a->q_scale_inv);
+    }
+    free(v32); free(x); free(o);
+}
 
 /* vLLM issue: DeepSeek R1 keeps q_rope / q_nope and k_rope / k_nope apart,
  * RoPE interleaved; concat_and_cache_mla stores [kv_c | rope(k_pe)] into
@@ -497,6 +542,7 @@ int oracle_mla_concat_rope_append(const oracle_mla_args *a)
 {
     int R = a->rope_dim, K = a->kv_lora_rank;
     if (R % 2) return ORC_BAD_ARGS;
+    if (a->q_mode < 0 || a->q_mode > 2) return ORC_BAD_ARGS;
     double *x = malloc(sizeof(double) * (size_t)R);
     double *o = malloc(sizeof(double) * (size_t)R);
     double *c = malloc(sizeof(double) * (size_t)R / 2);
@@ -510,11 +556,15 @@ int oracle_mla_concat_rope_append(const oracle_mla_args *a)
             c[i] = (double)a->cos_sin[pos * R + i];
             s[i] = (double)a->cos_sin[pos * R + R / 2 + i];
         }
-        for (int h = 0; h < a->H; ++h) {
-            uint16_t *qr = a->q + t * a->q_token_stride + (int64_t)h * a->q_head_stride + a->nope_dim;
-            for (int d = 0; d < R; ++d) x[d] = oracle_bf16_to_f64(qr[d]);
-            oracle_rope(x, R, a->rope, c, s, o);
-            for (int d = 0; d < R; ++d) qr[d] = oracle_f32_to_bf16((float)o[d]);
+        if (a->q_mode == 0) {
+            for (int h = 0; h < a->H; ++h) {
+                uint16_t *qr = a->q + t * a->q_token_stride + (int64_t)h * a->q_head_stride + a->nope_dim;
+                for (int d = 0; d < R; ++d) x[d] = oracle_bf16_to_f64(qr[d]);
+                oracle_rope(x, R, a->rope, c, s, o);
+                for (int d = 0; d < R; ++d) qr[d] = oracle_f32_to_bf16((float)o[d]);
+            }
+        } else {
+            mla_q_fp8(a, t, c, s);
         }
         const uint16_t *kp = a->k_pe + t * a->k_pe_stride;
         for (int d = 0; d < R; ++d) x[d] = oracle_bf16_to_f64(kp[d]);

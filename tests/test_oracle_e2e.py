@@ -427,3 +427,96 @@ def test_mla_concat_layout_and_values(fp8):
     for s in range(flat.shape[0]):
         if s not in written:
             assert np.array_equal(flat[s], flat0[s])
+
+
+# ----------------------------------------------------------------------------
+# MLA Q quantisation (FP8 q_out; the vLLM issue's static per-tensor and
+# dynamic per-token question, the FlashInfer MLA RoPE + quantize kernel)
+# ----------------------------------------------------------------------------
+
+def run_mla_q8(inp: W.MlaInputs):
+    out = {"q": inp.q.copy(), "kv_cache": inp.kv_cache0.copy(), "q_out": inp.q_out0.copy(),
+           "q_scale": None if inp.q_scale0 is None else inp.q_scale0.copy()}
+    oracle.mla_concat_rope_append(inp, out)
+    return out
+
+
+def _e4m3_grid_bits(rng, shape, lo_exp=-5, hi_exp=7):
+    """bf16 bits of random normal E4M3 values 2^e * (1 + m/8), e in [lo, hi]."""
+    e = rng.integers(lo_exp, hi_exp + 1, size=shape)
+    m = rng.integers(0, 8, size=shape)
+    sgn = np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+    v = sgn * np.ldexp(1.0 + m / 8.0, e)
+    return W.to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("q_scale_inv", [1.0, 0.5])
+def test_mla_static_fp8_q_of_grid_values_at_position_zero(q_scale_inv):
+    """At position 0 RoPE is the identity (cos 1, sin 0), so with inputs on
+    the E4M3 grid and a power-of-two static scale every code is exact: the
+    nope dims pass through, the rope dims too, and q stays untouched."""
+    inp = W.mla_case(seed=8, T=5, H=3, num_blocks=2, block_size=8, positions=np.zeros(5, np.int64),
+                     q_mode=W.Q_FP8_STATIC, q_scale_inv=q_scale_inv)
+    rng = np.random.default_rng(80)
+    inp.q = _e4m3_grid_bits(rng, inp.q.shape)
+    out = run_mla_q8(inp)
+    assert np.array_equal(out["q"], inp.q)
+    x = W.bf16_bits_to_f32(inp.q).astype(np.float64) * q_scale_inv
+    lut = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    assert np.array_equal(lut[out["q_out"]], x)
+
+
+def test_mla_dynamic_fp8_q_scale_spans_all_heads_of_a_token():
+    """One scale per token over every head: token 0 has a single 10.0 in head
+    2 and values <= 1 elsewhere, so s = fp32(10 / 448) for the whole token;
+    10.0 encodes to 448 (0x7E) and the other heads' codes use the same s."""
+    T, H = 3, 4
+    inp = W.mla_case(seed=9, T=T, H=H, num_blocks=2, block_size=8, positions=np.zeros(T, np.int64),
+                     q_mode=W.Q_FP8_DYNAMIC)
+    rng = np.random.default_rng(90)
+    vals = rng.uniform(-1.0, 1.0, size=inp.q.shape)
+    vals[0, 2, 17] = 10.0
+    vals[1] = 0.0                                  # all-zero token
+    inp.q = W.to_bf16_bits(vals)
+    out = run_mla_q8(inp)
+    s0 = out["q_scale"][0]
+    assert s0 == np.float32(10.0 / 448.0)
+    assert out["q_out"][0, 2, 17] == 0x7E
+    x0 = W.bf16_bits_to_f32(inp.q[0]).astype(np.float64)
+    assert np.array_equal(out["q_out"][0], oracle.f64_to_e4m3(x0 / np.float64(s0)))
+    assert out["q_scale"][1] == np.float32(1e-6 / 448.0)
+    assert not out["q_out"][1].any()
+    # no code above the top of the range
+    lut = np.array([abs(oracle.e4m3_to_f64(c)) if c not in (0x7F, 0xFF) else np.inf for c in range(256)])
+    assert lut[out["q_out"]].max() <= 448.0
+
+
+def test_mla_fp8_q_suppressed_token_writes_nothing():
+    inp = W.mla_case(seed=10, T=6, H=2, num_blocks=2, block_size=8, q_mode=W.Q_FP8_DYNAMIC)
+    inp.positions = inp.positions.copy()
+    inp.positions[4] = -1
+    out = run_mla_q8(inp)
+    assert np.array_equal(out["q_out"][4], inp.q_out0[4])
+    assert out["q_scale"][4].tobytes() == inp.q_scale0[4].tobytes()
+    assert not np.array_equal(out["q_out"][3], inp.q_out0[3])
+    assert np.array_equal(out["q"], inp.q)
+
+
+def test_mla_static_fp8_q_rotates_only_the_rope_slice():
+    """At non-zero positions the nope dims of E4M3-grid inputs still pass
+    through exactly (scale 1), and the rope dims are E4M3 of the pinned RoPE
+    of that slice rounded to fp32."""
+    inp = W.mla_case(seed=11, T=4, H=3, num_blocks=2, block_size=8, q_mode=W.Q_FP8_STATIC, rope=W.ROPE_NEOX)
+    rng = np.random.default_rng(110)
+    inp.q = _e4m3_grid_bits(rng, inp.q.shape)
+    out = run_mla_q8(inp)
+    N, R = inp.nope_dim, inp.rope_dim
+    lut = np.array([oracle.e4m3_to_f64(c) for c in range(256)])
+    x = W.bf16_bits_to_f32(inp.q).astype(np.float64)
+    assert np.array_equal(lut[out["q_out"][:, :, :N]], x[:, :, :N])
+    for t in range(inp.T):
+        pos = inp.positions[t]
+        c, s = inp.cos_sin[pos, :R // 2], inp.cos_sin[pos, R // 2:]
+        for h in range(inp.H):
+            o = oracle.rope(x[t, h, N:], W.ROPE_NEOX, c, s).astype(np.float32)
+            assert np.array_equal(out["q_out"][t, h, N:], oracle.f64_to_e4m3(o.astype(np.float64)))

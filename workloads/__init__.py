@@ -310,6 +310,11 @@ class MlaInputs:
     kv_scale: float
     kv_cache0: np.ndarray    # uint8/uint16 [num_blocks, block_size, kv_lora_rank + rope_dim]
     meta: dict = field(default_factory=dict)
+    q_mode: int = Q_BF16     # Q_BF16: RoPE in place in q; FP8 modes: E4M3 q_out, q read-only
+    q_scale_inv: float = 1.0
+    upper_max: float = 448.0
+    q_out0: np.ndarray | None = None    # uint8 [T, H, nope + rope] (FP8 Q modes)
+    q_scale0: np.ndarray | None = None  # fp32 [T] (dynamic)
 
     @property
     def row_elems(self) -> int:
@@ -320,21 +325,32 @@ class MlaInputs:
         elt = 1 if self.kv_fp8 else 2
         n_written = int(((self.slot_mapping >= 0) &
                          (self.slot_mapping < self.num_blocks * self.block_size)).sum())
-        d = {
-            "q_rope_read": T * H * R * 2,
-            "q_rope_write": T * H * R * 2,
+        if self.q_mode != Q_BF16:
+            W = self.nope_dim + R
+            d = {
+                "q_read": T * H * W * 2,
+                "q_write": T * H * W,
+                "q_scale": T * 4 if self.q_mode == Q_FP8_DYNAMIC else 0,
+            }
+        else:
+            d = {
+                "q_rope_read": T * H * R * 2,
+                "q_rope_write": T * H * R * 2,
+            }
+        d.update({
             "kv_c_read": T * K * 2,
             "k_pe_read": T * R * 2,
             "cos_sin": T * R * 4,
             "cache_write": n_written * (K + R) * elt,
-        }
+        })
         d["total"] = sum(d.values())
         return d
 
 
 def mla_case(*, name="custom", seed, T, H=128, nope_dim=128, rope_dim=64, kv_lora_rank=512,
              rope=ROPE_INTERLEAVED, theta=1e4, cs_rows=16384, num_blocks=128, block_size=64,
-             kv_fp8=True, kv_scale=0.02, negative_slots=0, positions=None) -> MlaInputs:
+             kv_fp8=True, kv_scale=0.02, negative_slots=0, positions=None, q_mode=Q_BF16,
+             q_scale_inv=1.0, upper_max=448.0) -> MlaInputs:
     rng = np.random.default_rng(seed)
     q = to_bf16_bits(rng.standard_normal((T, H, nope_dim + rope_dim)))
     kv_c = to_bf16_bits(rng.standard_normal((T, kv_lora_rank)))
@@ -350,11 +366,17 @@ def mla_case(*, name="custom", seed, T, H=128, nope_dim=128, rope_dim=64, kv_lor
     nbytes = num_blocks * block_size * (kv_lora_rank + rope_dim) * elt
     cache0 = sentinel_bytes(rng, nbytes).view(np.uint8 if kv_fp8 else np.uint16)
     cache0 = cache0.reshape(num_blocks, block_size, kv_lora_rank + rope_dim)
+    q_out0 = q_scale0 = None
+    if q_mode != Q_BF16:
+        q_out0 = sentinel_bytes(rng, T * H * (nope_dim + rope_dim)).reshape(T, H, nope_dim + rope_dim)
+        if q_mode == Q_FP8_DYNAMIC:
+            q_scale0 = sentinel_bytes(rng, T * 4).view(np.float32).copy()
     return MlaInputs(name=name, T=T, H=H, nope_dim=nope_dim, rope_dim=rope_dim,
                      kv_lora_rank=kv_lora_rank, q=q, kv_c=kv_c, k_pe=k_pe, rope=rope,
                      cos_sin=cos_sin, positions=np.asarray(positions, np.int64), slot_mapping=slots,
                      kv_fp8=kv_fp8, num_blocks=num_blocks, block_size=block_size,
-                     kv_scale=kv_scale, kv_cache0=cache0, meta={"seed": seed})
+                     kv_scale=kv_scale, kv_cache0=cache0, meta={"seed": seed}, q_mode=q_mode,
+                     q_scale_inv=q_scale_inv, upper_max=upper_max, q_out0=q_out0, q_scale0=q_scale0)
 
 
 # ----------------------------------------------------------------------------
