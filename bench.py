@@ -127,11 +127,15 @@ class MlaCall:
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(dt)
         self.q = up(inp.q, torch.int16)
         self.cache = up(inp.kv_cache0, torch.uint8)
+        sc = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)  # noqa: E731
+        self.q_out = None if inp.q_out0 is None else up(inp.q_out0, torch.uint8)
+        self.q_scale = None if inp.q_scale0 is None else up(inp.q_scale0, torch.float32)
         self.params = qp.mla_params(
             q=self.q, kv_c=up(inp.kv_c, torch.int16), k_pe=up(inp.k_pe, torch.int16),
             cos_sin_cache=up(inp.cos_sin, torch.float32), positions=up(inp.positions, torch.int64),
             slot_mapping=up(inp.slot_mapping, torch.int64), kv_cache=self.cache, num_q_heads=inp.H,
-            kv_scale=torch.tensor([inp.kv_scale], dtype=torch.float32, device=dev))
+            nope_dim=inp.nope_dim, kv_scale=sc(inp.kv_scale), q_mode=inp.q_mode, q_out=self.q_out,
+            q_scale=self.q_scale, q_scale_inv=sc(inp.q_scale_inv), upper_max=inp.upper_max)
         self.params.struct_size = ctypes.sizeof(self.params)
         self._ref = ctypes.byref(self.params)
         self._fn = qp.lib().qkprep_mla_concat_rope_append
@@ -141,6 +145,7 @@ class MlaCall:
     def launch(self):
         st = self._fn(self._ref, self._stream)
         if st != 0:
+            import paged_kv_cache_token_amd as qp
             raise qp.QkprepError(st)
 
 

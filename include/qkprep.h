@@ -224,6 +224,24 @@ typedef struct qkprep_mla_params {
     int32_t block_size;            /* >= 1 */
     int64_t block_stride;          /* elements, >= block_size * (kv_lora_rank + rope_dim) */
     const float* kv_scale;         /* device fp32 scalar (FP8 cache only) */
+
+    /* Q output.  Q_BF16: RoPE in place in q as above (the fields below are
+     * unused).  FP8_STATIC / FP8_DYNAMIC: q is read only and
+     *   q_out[t][h][0 : nope_dim + rope_dim] <- E4M3(v * q_scale_inv)      (static)
+     *                                        or E4M3(v / s_t)             (dynamic)
+     * with v = [q_nope | RoPE(q_rope)] in fp32 and, per token, one scale
+     * s_t = max(max |v| over all heads and dims, 1e-6) / upper_max stored at
+     * q_scale[t].  Needs nope_dim a multiple of 32 and at most 128; the
+     * dynamic mode needs num_q_heads <= 128.  A suppressed token writes
+     * neither q_out nor q_scale. */
+    int32_t q_mode;                /* qkprep_qmode */
+    void* q_out;                   /* E4M3 codes, (t, h, d) at t*q_out_token_stride + h*q_out_head_stride + d;
+                                      16-B aligned, must not overlap q */
+    int64_t q_out_token_stride;    /* multiple of 16 */
+    int64_t q_out_head_stride;     /* >= nope_dim + rope_dim, multiple of 16 */
+    float* q_scale;                /* FP8_DYNAMIC: fp32 [T] */
+    const float* q_scale_inv;      /* FP8_STATIC: device fp32 scalar */
+    float upper_max;               /* FP8_DYNAMIC: finite, in (0, 448] */
 } qkprep_mla_params;
 
 /* Host checks, then one kernel launch on `stream` (none when there is no

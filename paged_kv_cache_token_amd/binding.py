@@ -66,6 +66,8 @@ class MlaParams(ctypes.Structure):
         ("slot_mapping", _vp),
         ("kv_cache", _vp), ("kv_dtype", _i32), ("num_blocks", _i64), ("block_size", _i32),
         ("block_stride", _i64), ("kv_scale", _vp),
+        ("q_mode", _i32), ("q_out", _vp), ("q_out_token_stride", _i64), ("q_out_head_stride", _i64),
+        ("q_scale", _vp), ("q_scale_inv", _vp), ("upper_max", ctypes.c_float),
     ]
 
 
@@ -204,7 +206,9 @@ def qkprep_norm_rope_append(stream=None, **kw) -> None:
 
 def mla_params(*, q, kv_c, k_pe, cos_sin_cache, positions, slot_mapping, kv_cache, num_q_heads,
                nope_dim=128, rope_dim=64, kv_lora_rank=512, rope=ROPE_INTERLEAVED, kv_dtype=FP8_E4M3,
-               kv_scale=None, num_tokens=None, q_token_stride=None, q_head_stride=None) -> MlaParams:
+               kv_scale=None, num_tokens=None, q_token_stride=None, q_head_stride=None, q_mode=Q_BF16,
+               q_out=None, q_out_token_stride=None, q_out_head_stride=None, q_scale=None, q_scale_inv=None,
+               upper_max=448.0) -> MlaParams:
     p = MlaParams()
     p.num_tokens = q.shape[0] if num_tokens is None else num_tokens
     p.num_q_heads, p.nope_dim, p.rope_dim, p.kv_lora_rank = num_q_heads, nope_dim, rope_dim, kv_lora_rank
@@ -219,11 +223,18 @@ def mla_params(*, q, kv_c, k_pe, cos_sin_cache, positions, slot_mapping, kv_cach
     p.kv_cache, p.kv_dtype = _ptr(kv_cache), kv_dtype
     p.num_blocks, p.block_size, p.block_stride = kv_cache.shape[0], kv_cache.shape[1], kv_cache.stride(0)
     p.kv_scale = _ptr(kv_scale)
+    p.q_mode = q_mode
+    p.q_out = _ptr(q_out)
+    if q_out is not None:
+        p.q_out_token_stride = q_out.stride(0) if q_out_token_stride is None else q_out_token_stride
+        p.q_out_head_stride = q_out.stride(1) if q_out_head_stride is None else q_out_head_stride
+    p.q_scale, p.q_scale_inv, p.upper_max = _ptr(q_scale), _ptr(q_scale_inv), upper_max
     return p
 
 
 def qkprep_mla_concat_rope_append(stream=None, **kw) -> None:
-    """MLA: RoPE on q's rope slice in place + [kv_c | RoPE(k_pe)] into the latent cache."""
+    """MLA: RoPE on q's rope slice in place (or [q_nope | RoPE(q_rope)] as E4M3
+    into q_out) + [kv_c | RoPE(k_pe)] into the latent cache."""
     st = call_mla_concat_rope_append(mla_params(**kw), stream)
     if st != QKPREP_OK:
         raise QkprepError(st)

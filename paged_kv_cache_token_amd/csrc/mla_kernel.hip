@@ -278,10 +278,215 @@ hipError_t launch_t(const MlaDevArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// FP8 Q modes: [q_nope | RoPE(q_rope)] -> E4M3 q_out (q read only) with a
+// static per-tensor scale, or with one dynamic scale per token over all of
+// its heads (vLLM issue: static per-tensor / dynamic per-token quantisation
+// of the MLA query next to the FlashInfer MLA RoPE + quantize kernel).
+//
+// A workgroup takes whole tokens (t = blockIdx.x, + grid, ...), so the
+// token's amax is one workgroup reduction (one barrier).  Four lanes own a
+// head: lane l loads the NV = nope_dim / 32 nope vectors [8 l NV, 8 (l+1) NV)
+// and the rope vectors [8l, 8l+8), [32 + 8l, 32 + 8l + 8); a wave covers 16
+// heads, a workgroup 64 per round, and two rounds (128 heads) are held in
+// registers.  The token's cos/sin values are read straight into registers
+// (every head uses the same 16 per lane).  One wave also writes the
+// token's latent cache row.
+// ---------------------------------------------------------------------------
+constexpr int kQ8Rounds = 2;
+
+template <int QMODE, bool KVFP8>
+__global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs a) {
+    typedef typename std::conditional<KVFP8, uint8_t, uint16_t>::type kv_t;
+    __shared__ float s_amax[2][4];
+
+    preload_kernargs(a);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int grp = lane / kLanesPerHead;
+    const int gl = lane % kLanesPerHead;
+    const int N = a.nope_dim;
+    const int NV = N >> 5;
+    const int K = a.kv_lora_rank;
+    const int row_len = K + kRope;
+    const int rounds = (a.H + 63) >> 6;
+    const float q_static = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
+    const float inv_um = (QMODE == 1) ? 1.0f / a.upper_max : 1.0f;
+    const float inv_kv = KVFP8 ? 1.0f / *a.kv_scale : 1.0f;
+    kv_t* cache = reinterpret_cast<kv_t*>(a.kv_cache);
+    int par = 0;   // s_amax slot: consecutive reductions alternate, so one barrier each suffices
+
+    for (int64_t t = blockIdx.x; t < a.T; t += a.grid) {
+        const int64_t pos = a.positions[t];
+        if (pos < 0 || pos >= a.cs_rows) continue;     // suppressed token (same for the whole workgroup)
+        const int64_t slot = a.slot_mapping[t];
+        const uint16_t* qt = a.q + t * a.q_token_stride;
+        uint8_t* ot = a.q_out + t * a.q_out_token_stride;
+        const bool latent = wave == (int)(t & 3);
+        uint4 kvv = make_uint4(0, 0, 0, 0), pe = make_uint4(0, 0, 0, 0);
+        if (latent) {
+            kvv = ld16(a.kv_c + t * a.kv_c_stride + 8 * lane);
+            pe = ld16(a.k_pe + t * a.k_pe_stride + 8 * (lane & 7));
+        }
+        float c[8], s[8];
+        lane_cos_sin(a.cos_sin + pos * kRope, gl, a.rope, c, s);
+
+        for (int r0 = 0; r0 < rounds; r0 += kQ8Rounds) {
+            uint4 vn[kQ8Rounds][4], vr[kQ8Rounds][2];
+            int hh[kQ8Rounds];
+#pragma unroll
+            for (int k = 0; k < kQ8Rounds; ++k) {
+                const int h = (r0 + k) * 64 + wave * kHeadsPerWave + grp;
+                hh[k] = h;
+                const uint16_t* qh = qt + (int64_t)(h < a.H ? h : 0) * a.q_head_stride;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vn[k][j] = j < NV ? ld16(qh + 8 * (gl * NV + j)) : make_uint4(0, 0, 0, 0);
+                vr[k][0] = ld16(qh + N + 8 * gl);
+                vr[k][1] = ld16(qh + N + kHalf + 8 * gl);
+            }
+            float xr[kQ8Rounds][16];
+            float amax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < kQ8Rounds; ++k) {
+                unpack8(vr[k][0], xr[k]);
+                unpack8(vr[k][1], xr[k] + 8);
+                rope16(xr[k], c, s, a.rope);
+                if (QMODE == 1 && hh[k] < a.H) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(xr[k][i]));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float x[8];
+                        unpack8(vn[k][j], x);   // zero vectors past NV
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+                    }
+                }
+            }
+            float mul = q_static;
+            if constexpr (QMODE == 1) {
+                amax = group_max<16>(amax);
+                amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
+                amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+                if (lane == 0) s_amax[par][wave] = amax;
+                __syncthreads();
+                const float m = __builtin_fmaxf(__builtin_fmaxf(s_amax[par][0], s_amax[par][1]),
+                                                __builtin_fmaxf(s_amax[par][2], s_amax[par][3]));
+                par ^= 1;
+                // s = max(amax, 1e-6) / upper_max; payload = v * (1 / s)
+                const float sc = __builtin_fmaxf(m, 1e-6f) * inv_um;
+                mul = __builtin_amdgcn_rcpf(sc);
+                if (tid == 0) a.q_scale[t] = sc;
+            }
+#pragma unroll
+            for (int k = 0; k < kQ8Rounds; ++k) {
+                if (hh[k] >= a.H) continue;   // whole 4-lane group skips together
+                uint8_t* oh = ot + (int64_t)hh[k] * a.q_out_head_stride;
+                if ((NV & 1) == 0) {
+#pragma unroll
+                    for (int j = 0; j < 4; j += 2) {
+                        if (j < NV) {
+                            float x[16];
+                            unpack8(vn[k][j], x);
+                            unpack8(vn[k][j + 1], x + 8);
+                            const uint2 lo = pack8_fp8(x, mul), hi = pack8_fp8(x + 8, mul);
+                            st16(oh + 8 * (gl * NV + j), make_uint4(lo.x, lo.y, hi.x, hi.y));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (j < NV) {
+                            float x[8];
+                            unpack8(vn[k][j], x);
+                            st8(oh + 8 * (gl * NV + j), pack8_fp8(x, mul));
+                        }
+                    }
+                }
+                store_fp8_row(oh + N, gl, kHalf, pack8_fp8(xr[k], mul), pack8_fp8(xr[k] + 8, mul));
+            }
+        }
+
+        if (latent) {
+            // k_pe second halves come from lanes 4..7 (all lanes of the wave take part)
+            uint4 pe_hi;
+            pe_hi.x = __shfl(pe.x, lane + 4, 64);
+            pe_hi.y = __shfl(pe.y, lane + 4, 64);
+            pe_hi.z = __shfl(pe.z, lane + 4, 64);
+            pe_hi.w = __shfl(pe.w, lane + 4, 64);
+            if (slot >= 0 && slot < a.capacity) {
+                kv_t* dst = cache + (slot / a.block_size) * a.block_stride + (slot % a.block_size) * (int64_t)row_len;
+                if constexpr (KVFP8) {
+                    float x[8];
+                    unpack8(kvv, x);
+                    st8(dst + 8 * lane, pack8_fp8(x, inv_kv));
+                } else {
+                    st16(dst + 8 * lane, kvv);
+                }
+                for (int e = 512 + 8 * lane; e < K; e += 512) {
+                    const uint4 v = ld16(a.kv_c + t * a.kv_c_stride + e);
+                    if constexpr (KVFP8) {
+                        float x[8];
+                        unpack8(v, x);
+                        st8(dst + e, pack8_fp8(x, inv_kv));
+                    } else {
+                        st16(dst + e, v);
+                    }
+                }
+                if (lane < kLanesPerHead) {
+                    float x[16];
+                    unpack8(pe, x);
+                    unpack8(pe_hi, x + 8);
+                    rope16(x, c, s, a.rope);
+                    if constexpr (KVFP8) {
+                        store_fp8_row(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf, pack8_fp8(x, inv_kv),
+                                      pack8_fp8(x + 8, inv_kv));
+                    } else {
+                        st16(dst + K + 8 * gl, pack8_bf16(x));
+                        st16(dst + K + kHalf + 8 * gl, pack8_bf16(x + 8));
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int QMODE, bool KVFP8>
+int q8_resident_blocks() {
+    static int cached_dev = -1, cached = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev != cached_dev) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mla_q8_kernel<QMODE, KVFP8>, kBlockThreads, 0) !=
+            hipSuccess)
+            per_cu = 1;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+        cached = (per_cu < 1 ? 1 : per_cu) * cus;
+        cached_dev = dev;
+    }
+    return cached;
+}
+
+template <int QMODE, bool KVFP8>
+hipError_t launch_q8_t(const MlaDevArgs& a, hipStream_t stream) {
+    MlaDevArgs la = a;
+    const int64_t cap = q8_resident_blocks<QMODE, KVFP8>();
+    la.grid = (int)(a.T < cap ? a.T : cap);
+    hipLaunchKernelGGL((mla_q8_kernel<QMODE, KVFP8>), dim3(la.grid), dim3(kBlockThreads), 0, stream, la);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_mla_concat_rope(const MlaDevArgs& a, int kv_fp8, hipStream_t stream) {
     return kv_fp8 ? launch_t<true>(a, stream) : launch_t<false>(a, stream);
+}
+
+hipError_t launch_mla_q8(const MlaDevArgs& a, int kv_fp8, hipStream_t stream) {
+    if (a.q_mode == 1) return kv_fp8 ? launch_q8_t<1, true>(a, stream) : launch_q8_t<1, false>(a, stream);
+    return kv_fp8 ? launch_q8_t<2, true>(a, stream) : launch_q8_t<2, false>(a, stream);
 }
 
 }  // namespace qkprep

@@ -157,7 +157,22 @@ qkprep_status qkprep_mla_concat_rope_append(const qkprep_mla_params* p, hipStrea
     if (p->kv_lora_rank <= 0 || p->kv_lora_rank % 512) return QKPREP_E_UNSUPPORTED;
     if (p->rope < 0 || p->rope > 1 || p->kv_dtype < 0 || p->kv_dtype > 1) return QKPREP_E_RANGE;
     if (p->block_size <= 0) return QKPREP_E_RANGE;
+    if (p->q_mode < 0 || p->q_mode > 2) return QKPREP_E_RANGE;
+    const bool q8 = p->q_mode != QKPREP_Q_BF16;
+    if (q8 && (p->nope_dim % 32 || p->nope_dim > 128)) return QKPREP_E_UNSUPPORTED;
+    if (p->q_mode == QKPREP_Q_FP8_DYNAMIC) {
+        if (p->num_q_heads > 128) return QKPREP_E_UNSUPPORTED;
+        if (!(p->upper_max > 0.0f && p->upper_max <= 448.0f)) return QKPREP_E_RANGE;
+    }
     if (T == 0) return QKPREP_OK;
+    if (q8) {
+        if (!p->q_out) return QKPREP_E_NULL;
+        if (p->q_mode == QKPREP_Q_FP8_DYNAMIC && !p->q_scale) return QKPREP_E_NULL;
+        if (p->q_mode == QKPREP_Q_FP8_STATIC && !p->q_scale_inv) return QKPREP_E_NULL;
+        if (p->q_out_head_stride < p->nope_dim + p->rope_dim) return QKPREP_E_SHAPE;
+        if (p->q_out_token_stride % 16 || p->q_out_head_stride % 16 || !aligned16(p->q_out))
+            return QKPREP_E_ALIGN;
+    }
     if (!p->q || !p->kv_c || !p->k_pe || !p->cos_sin_cache || !p->positions || !p->slot_mapping ||
         !p->kv_cache)
         return QKPREP_E_NULL;
@@ -188,10 +203,14 @@ qkprep_status qkprep_mla_concat_rope_append(const qkprep_mla_params* p, hipStrea
     a.capacity = p->num_blocks * (int64_t)p->block_size;
     a.block_size = p->block_size; a.block_stride = p->block_stride;
     a.kv_scale = p->kv_scale;
+    a.q_mode = p->q_mode;
+    a.q_out = static_cast<uint8_t*>(p->q_out);
+    a.q_out_token_stride = p->q_out_token_stride; a.q_out_head_stride = p->q_out_head_stride;
+    a.q_scale = p->q_scale; a.q_scale_inv = p->q_scale_inv; a.upper_max = p->upper_max;
     a.chunks_per_token = (a.H + 15) / 16 + 1;
     a.tokens_per_tile = kMaxTokensPerTile;
     a.total_items = (int64_t)T * a.chunks_per_token;
-    hipError_t e = launch_mla_concat_rope(a, p->kv_dtype, stream);
+    hipError_t e = q8 ? launch_mla_q8(a, p->kv_dtype, stream) : launch_mla_concat_rope(a, p->kv_dtype, stream);
     return e == hipSuccess ? QKPREP_OK : QKPREP_E_LAUNCH;
 }
 

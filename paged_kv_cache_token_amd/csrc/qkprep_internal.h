@@ -87,6 +87,13 @@ struct MlaDevArgs {
     int32_t block_size;
     int64_t block_stride;
     const float* kv_scale;
+    // FP8 Q output (q_mode 1 dynamic per token, 2 static)
+    int32_t q_mode;
+    uint8_t* q_out;
+    int64_t q_out_token_stride, q_out_head_stride;
+    float* q_scale;
+    const float* q_scale_inv;
+    float upper_max;
     // geometry: balanced contiguous ranges of the T * chunks_per_token items
     int32_t tokens_per_tile;            // most tokens staged in LDS at once
     int32_t chunks_per_token;           // ceil(H / heads per wave) + 1 latent chunk
@@ -98,5 +105,7 @@ struct MlaDevArgs {
 hipError_t launch_norm_rope_append(const NraDevArgs& a, int head_dim, int q_mode, int kv_fp8,
                                    hipStream_t stream);
 hipError_t launch_mla_concat_rope(const MlaDevArgs& a, int kv_fp8, hipStream_t stream);
+// FP8 Q modes: one workgroup per token at a time
+hipError_t launch_mla_q8(const MlaDevArgs& a, int kv_fp8, hipStream_t stream);
 
 }  // namespace qkprep

@@ -357,26 +357,46 @@ class DeviceMla:
         cdt = torch.uint8 if inp.kv_fp8 else torch.int16
         self.cache = Guarded(inp.kv_cache0.nbytes, cdt, inp.kv_cache0.shape, init=inp.kv_cache0)
         self.kv_scale = _scalar(inp.kv_scale)
+        self.q_out = self.q_scale = None
+        if inp.q_out0 is not None:
+            self.q_out = Guarded(inp.q_out0.nbytes, torch.uint8, inp.q_out0.shape, init=inp.q_out0)
+        if inp.q_scale0 is not None:
+            self.q_scale = Guarded(inp.q_scale0.nbytes, torch.float32, inp.q_scale0.shape, init=inp.q_scale0)
+        self.q_scale_inv = _scalar(inp.q_scale_inv)
 
-    def run(self, stream=None):
+    def kwargs(self) -> dict:
         inp = self.inp
-        qp.qkprep_mla_concat_rope_append(
-            stream=stream, q=self.q.t, kv_c=self.kv_c, k_pe=self.k_pe.t, cos_sin_cache=self.cos_sin,
+        return dict(
+            q=self.q.t, kv_c=self.kv_c, k_pe=self.k_pe.t, cos_sin_cache=self.cos_sin,
             positions=self.positions, slot_mapping=self.slots, kv_cache=self.cache.t, num_q_heads=inp.H,
             nope_dim=inp.nope_dim, rope_dim=inp.rope_dim, kv_lora_rank=inp.kv_lora_rank, rope=inp.rope,
-            kv_dtype=qp.FP8_E4M3 if inp.kv_fp8 else qp.BF16, kv_scale=self.kv_scale)
+            kv_dtype=qp.FP8_E4M3 if inp.kv_fp8 else qp.BF16, kv_scale=self.kv_scale, q_mode=inp.q_mode,
+            q_out=None if self.q_out is None else self.q_out.t,
+            q_scale=None if self.q_scale is None else self.q_scale.t, q_scale_inv=self.q_scale_inv,
+            upper_max=inp.upper_max)
+
+    def run(self, stream=None):
+        qp.qkprep_mla_concat_rope_append(stream=stream, **self.kwargs())
 
     def guards_intact(self):
-        return self.q.guards_intact() and self.cache.guards_intact() and self.k_pe.guards_intact()
+        bufs = [self.q, self.cache, self.k_pe, self.q_out, self.q_scale]
+        return all(b.guards_intact() for b in bufs if b is not None)
 
     def host_outputs(self):
         cdt = np.uint8 if self.inp.kv_fp8 else np.uint16
-        return {"q": self.q.t.cpu().numpy().view(np.uint16), "kv_cache": self.cache.t.cpu().numpy().view(cdt),
-                "k_pe": self.k_pe.t.cpu().numpy().view(np.uint16)}
+        out = {"q": self.q.t.cpu().numpy().view(np.uint16), "kv_cache": self.cache.t.cpu().numpy().view(cdt),
+               "k_pe": self.k_pe.t.cpu().numpy().view(np.uint16)}
+        if self.q_out is not None:
+            out["q_out"] = self.q_out.t.cpu().numpy().view(np.uint8)
+        if self.q_scale is not None:
+            out["q_scale"] = self.q_scale.t.cpu().numpy().view(np.float32)
+        return out
 
 
 def oracle_mla(inp: W.MlaInputs) -> dict:
-    out = {"q": inp.q.copy(), "kv_cache": inp.kv_cache0.copy()}
+    out = {"q": inp.q.copy(), "kv_cache": inp.kv_cache0.copy(),
+           "q_out": None if inp.q_out0 is None else inp.q_out0.copy(),
+           "q_scale": None if inp.q_scale0 is None else inp.q_scale0.copy()}
     oracle.mla_concat_rope_append(inp, out)
     return out
 
@@ -387,10 +407,23 @@ def compare_mla(inp: W.MlaInputs, gpu: dict, ref: dict) -> dict:
     rows = inp.cos_sin.shape[0]
     live = (inp.positions >= 0) & (inp.positions < rows)
     check_exact(gpu["k_pe"], inp.k_pe, "k_pe (read only)")
-    check_exact(gpu["q"][:, :, :nope], ref["q"][:, :, :nope], "q_nope")
-    if live.any():
-        check_bf16(gpu["q"][live][:, :, nope:nope + R], ref["q"][live][:, :, nope:nope + R], "q_rope", stats)
-    check_exact(gpu["q"][~live], ref["q"][~live], "q of suppressed tokens")
+    if inp.q_mode == W.Q_BF16:
+        check_exact(gpu["q"][:, :, :nope], ref["q"][:, :, :nope], "q_nope")
+        if live.any():
+            check_bf16(gpu["q"][live][:, :, nope:nope + R], ref["q"][live][:, :, nope:nope + R], "q_rope", stats)
+        check_exact(gpu["q"][~live], ref["q"][~live], "q of suppressed tokens")
+    else:
+        check_exact(gpu["q"], inp.q, "q (read only in the FP8 Q modes)")
+        if live.any():
+            check_e4m3(gpu["q_out"][live], ref["q_out"][live], "q_out codes", stats)
+        check_exact(gpu["q_out"][~live], ref["q_out"][~live], "q_out of suppressed tokens")
+        if inp.q_mode == W.Q_FP8_DYNAMIC:
+            sg, sr = gpu["q_scale"], ref["q_scale"]
+            if live.any():
+                rel = np.abs(sg[live].astype(np.float64) - sr[live]) / np.abs(sr[live].astype(np.float64))
+                stats["q_scale"] = {"n": int(live.sum()), "max_rel": float(rel.max())}
+                assert rel.max() <= 1e-5, f"q_scale relative error {rel.max()}"
+            check_exact(sg[~live], sr[~live], "q_scale of suppressed tokens")
     cap = inp.num_blocks * inp.block_size
     s = inp.slot_mapping
     ok = live & (s >= 0) & (s < cap)

@@ -142,6 +142,22 @@ def test_mla_host_checks():
     assert st(nope_dim=4) == 4
     assert st(block_stride=100) == 2
     assert st(num_tokens=0, q=None) == 0
+    # FP8 Q modes
+    q8 = dict(q_out=0x9000, q_out_token_stride=128 * 192, q_out_head_stride=192, q_scale=0xA000,
+              q_scale_inv=0xB000)
+    assert st(q_mode=3, **q8) == 5
+    assert st(q_mode=2, nope_dim=72, q_head_stride=136, **q8) == 3
+    assert st(q_mode=2, nope_dim=160, q_head_stride=224, **q8) == 3
+    assert st(q_mode=1, num_q_heads=129, **q8) == 3
+    assert st(q_mode=1, upper_max=0.0, **q8) == 5
+    assert st(q_mode=1, upper_max=449.0, **q8) == 5
+    assert st(q_mode=1, upper_max=448.0, **dict(q8, q_out=None)) == 1
+    assert st(q_mode=1, upper_max=448.0, **dict(q8, q_scale=None)) == 1
+    assert st(q_mode=2, **dict(q8, q_scale_inv=None)) == 1
+    assert st(q_mode=2, **dict(q8, q_out_head_stride=184)) == 2
+    assert st(q_mode=2, **dict(q8, q_out_head_stride=200)) == 4
+    assert st(q_mode=2, **dict(q8, q_out=0x9008)) == 4
+    assert st(q_mode=1, num_tokens=0, upper_max=448.0, q=None, **q8) == 0
 
 
 def test_status_strings():

@@ -296,6 +296,43 @@ def test_mla_variants(fp8, rope, H_):
     H.compare_mla(inp, dev.host_outputs(), H.oracle_mla(inp))
 
 
+def _run_mla(inp):
+    dev = H.DeviceMla(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    return H.compare_mla(inp, dev.host_outputs(), H.oracle_mla(inp))
+
+
+@pytest.mark.parametrize("q_mode", [W.Q_FP8_DYNAMIC, W.Q_FP8_STATIC])
+def test_mla_fp8_q_full_size(q_mode):
+    """The 4096-token, 128-head MLA workload with Q quantised into an E4M3
+    q_out: one dynamic scale per token over all heads, or a static scale."""
+    inp = W.c5_mla(q_mode=q_mode, q_scale_inv=0.75)
+    print(_run_mla(inp), flush=True)
+
+
+# nope_dim multiple of 32 up to 128 (odd nope-vector counts store 8-byte
+# pieces), head counts below, at and above a 64-head round, both caches
+@pytest.mark.parametrize("q_mode", [W.Q_FP8_DYNAMIC, W.Q_FP8_STATIC])
+@pytest.mark.parametrize("H_,nope", [(128, 128), (16, 64), (20, 96), (100, 32), (3, 0), (64, 128)])
+@pytest.mark.parametrize("fp8", [True, False])
+def test_mla_fp8_q_variants(q_mode, H_, nope, fp8):
+    inp = W.mla_case(seed=H_ + nope + q_mode, T=61, H=H_, nope_dim=nope, num_blocks=8, block_size=16,
+                     kv_fp8=fp8, rope=W.ROPE_NEOX if H_ % 2 else W.ROPE_INTERLEAVED, negative_slots=3,
+                     q_mode=q_mode, q_scale_inv=2.0, upper_max=448.0 if fp8 else 240.0)
+    inp.positions = inp.positions.copy()
+    inp.positions[[0, 7]] = [-1, inp.cos_sin.shape[0]]
+    _run_mla(inp)
+
+
+def test_mla_static_fp8_q_more_than_two_rounds_of_heads():
+    # 200 heads: the static mode walks 64-head rounds two at a time
+    inp = W.mla_case(seed=200, T=19, H=200, num_blocks=4, block_size=16, q_mode=W.Q_FP8_STATIC,
+                     q_scale_inv=1.5)
+    _run_mla(inp)
+
+
 # ----------------------------------------------------------------------------
 # determinism, idempotency, graph capture
 # ----------------------------------------------------------------------------
