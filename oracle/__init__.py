@@ -165,6 +165,9 @@ class _NraArgs(ctypes.Structure):
         ("q_scale_inv", ctypes.c_float), ("upper_max", ctypes.c_float),
         ("k_out", ctypes.c_void_p), ("k_out_row_stride", ctypes.c_int64),
         ("flags", ctypes.c_void_p),
+        ("out_k", ctypes.c_void_p), ("out_v", ctypes.c_void_p), ("out_kv_row_stride", ctypes.c_int64),
+        ("kv_scale_mode", ctypes.c_int32), ("kv_group_size", ctypes.c_int32),
+        ("k_scale_out", ctypes.c_void_p), ("v_scale_out", ctypes.c_void_p),
     ]
 
 
@@ -263,6 +266,16 @@ def norm_rope_append(inp, out) -> NraResult:
         a.k_out_row_stride = inp.qkv_row_stride
     if out.get("flags") is not None:
         a.flags = _ptr(_need(out["flags"], np.int32))
+    kdt = np.uint8 if inp.kv_fp8 else np.uint16
+    if inp.kv_redirect:
+        a.out_k = _ptr(_need(out["out_k"], kdt))
+        a.out_v = _ptr(_need(out["out_v"], kdt))
+        a.out_kv_row_stride = inp.Hkv * D
+    a.kv_scale_mode = inp.kv_scale_mode
+    a.kv_group_size = inp.kv_group_size
+    if inp.kv_scale_mode:
+        a.k_scale_out = _ptr(_need(out["k_scale_out"], np.float32))
+        a.v_scale_out = _ptr(_need(out["v_scale_out"], np.float32))
     rc = lib().oracle_norm_rope_append(ctypes.byref(a))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")

@@ -270,6 +270,16 @@ typedef struct {
     int64_t k_out_row_stride;
     /* [B, Hkv] */
     int32_t *flags;
+    /* K/V redirect: when out_k != NULL the K / V rows of token t go to row t
+     * of out_k / out_v (row stride in elements) instead of the caches */
+    void *out_k, *out_v;
+    int64_t out_kv_row_stride;
+    /* FP8 K/V scales: 0 the static scalars k_scale / v_scale; 1 one dynamic
+     * scale per (token, kv head); 2 one per kv_group_size consecutive dims.
+     * Dynamic scales go to k_scale_out / v_scale_out, [cache row][Hkv][D/g]
+     * (cache row = page * page_size + row, or t when redirected). */
+    int32_t kv_scale_mode, kv_group_size;
+    float *k_scale_out, *v_scale_out;
 } oracle_nra_args;
 
 /* The contract's metadata validation (FlashInfer "Contract": malformed
@@ -333,20 +343,54 @@ static void store_q(const oracle_nra_args *a, int64_t t, int h, int64_t b, int64
     }
 }
 
-static void store_kv(const oracle_nra_args *a, void *cache, int64_t page_stride, int64_t page,
-                     int64_t row, int kh, const float *v32, const uint16_t *raw, float scale)
+/* Dims per K/V scale: the whole head row (static scalars, per-token mode)
+ * or kv_group_size. */
+static int kv_group(const oracle_nra_args *a)
+{
+    return a->kv_scale_mode == 2 ? a->kv_group_size : a->D;
+}
+
+/* Store one K or V head row.  v32 holds the encoded values as fp32 (K:
+ * normalised and rotated; V: the raw bf16 values, exact).  The row goes to
+ * the cache cell (page, row), or to row t of out_k / out_v when the call
+ * redirects K/V (FlashInfer "Contract": caller-owned out_k / out_v).
+ *   bf16 cache: RNE of v32 (for V a bit copy of raw)
+ *   FP8, static scale: E4M3(v32 / scale)
+ *   FP8, dynamic scales (the vLLM issue's dynamic per-token and per-group
+ *   question): for each group of g dims s = fp32(max(amax, 1e-6) / 448),
+ *   E4M3(v32 / s), s stored in the scale array at the row's entry. */
+static void store_kv(const oracle_nra_args *a, int is_v, int64_t t, int64_t page, int64_t row, int kh,
+                     const float *v32, const uint16_t *raw)
 {
     int D = a->D;
-    int64_t off = page * page_stride + (row * a->Hkv + kh) * (int64_t)D;
-    if (a->kv_fp8) {
-        uint8_t *dst = (uint8_t *)cache + off;
-        for (int d = 0; d < D; ++d) {
-            double x = raw ? oracle_bf16_to_f64(raw[d]) : (double)v32[d];
-            dst[d] = oracle_f64_to_e4m3(x / (double)scale);
-        }
+    int64_t esz = a->kv_fp8 ? 1 : 2;
+    char *dst;
+    int64_t srow;
+    if (a->out_k) {
+        dst = (char *)(is_v ? a->out_v : a->out_k) + (t * a->out_kv_row_stride + (int64_t)kh * D) * esz;
+        srow = t;
     } else {
-        uint16_t *dst = (uint16_t *)cache + off;
-        for (int d = 0; d < D; ++d) dst[d] = raw ? raw[d] : oracle_f32_to_bf16(v32[d]);
+        int64_t ps = is_v ? a->v_page_stride : a->k_page_stride;
+        dst = (char *)(is_v ? a->v_cache : a->k_cache) + (page * ps + (row * a->Hkv + kh) * (int64_t)D) * esz;
+        srow = page * a->page_size + row;
+    }
+    if (!a->kv_fp8) {
+        uint16_t *d16 = (uint16_t *)dst;
+        for (int d = 0; d < D; ++d) d16[d] = raw ? raw[d] : oracle_f32_to_bf16(v32[d]);
+        return;
+    }
+    uint8_t *d8 = (uint8_t *)dst;
+    if (a->kv_scale_mode == 0) {
+        double scale = (double)(is_v ? a->v_scale : a->k_scale);
+        for (int d = 0; d < D; ++d) d8[d] = oracle_f64_to_e4m3((double)v32[d] / scale);
+        return;
+    }
+    int g = kv_group(a), ng = D / g;
+    float *sc = (is_v ? a->v_scale_out : a->k_scale_out) + (srow * a->Hkv + kh) * ng;
+    for (int k = 0; k < ng; ++k) {
+        float s = oracle_q_scale(v32 + k * g, g, 448.0);
+        sc[k] = s;
+        for (int d = k * g; d < (k + 1) * g; ++d) d8[d] = oracle_f64_to_e4m3((double)v32[d] / (double)s);
     }
 }
 
@@ -386,18 +430,18 @@ static void nra_token(const oracle_nra_args *a, int64_t t, int64_t b, int64_t j,
             store_q(a, t, h, b, j, v32);
         } else {
             int kh = h - Hq;
-            if (page >= 0)
-                store_kv(a, a->k_cache, a->k_page_stride, page, row, kh, v32, NULL, a->k_scale);
+            if (page >= 0 || a->out_k) store_kv(a, 0, t, page, row, kh, v32, NULL);
             if (a->k_out) {
                 uint16_t *ko = a->k_out + t * a->k_out_row_stride + (int64_t)kh * D;
                 for (int d = 0; d < D; ++d) ko[d] = oracle_f32_to_bf16(v32[d]);
             }
         }
     }
-    if (page >= 0) {
+    if (page >= 0 || a->out_k) {
         for (int vh = 0; vh < Hkv; ++vh) {
             memcpy(raw, tok + (int64_t)(Hq + Hkv + vh) * D, sizeof(uint16_t) * (size_t)D);
-            store_kv(a, a->v_cache, a->v_page_stride, page, row, vh, NULL, raw, a->v_scale);
+            for (int d = 0; d < D; ++d) v32[d] = (float)oracle_bf16_to_f64(raw[d]);
+            store_kv(a, 1, t, page, row, vh, v32, raw);
         }
     }
     free(tok); free(x); free(y); free(o); free(c); free(s); free(v32); free(raw);
@@ -415,6 +459,10 @@ static int position_out_of_table(const oracle_nra_args *a, int64_t t)
 int oracle_norm_rope_append(const oracle_nra_args *a)
 {
     if (a->D % 2 || a->rot % 2 || a->rot < 0 || a->rot > a->D) return ORC_BAD_ARGS;
+    if (a->kv_scale_mode < 0 || a->kv_scale_mode > 2) return ORC_BAD_ARGS;
+    if (a->kv_scale_mode && (!a->kv_fp8 || !a->k_scale_out || !a->v_scale_out)) return ORC_BAD_ARGS;
+    if (a->kv_scale_mode == 2 && (a->kv_group_size <= 0 || a->D % a->kv_group_size)) return ORC_BAD_ARGS;
+    if ((a->out_k == NULL) != (a->out_v == NULL)) return ORC_BAD_ARGS;
     if (a->addressing == 0) {
         int bad = nra_invalid(a);
         if (a->flags)
@@ -432,7 +480,9 @@ int oracle_norm_rope_append(const oracle_nra_args *a)
                 nra_token(a, t, b, j, pos, page, L % a->page_size);
             }
         }
-        if (a->zero_tail) {
+        /* no tail clear when K/V are redirected (FlashInfer review: the
+         * caches are not touched then) */
+        if (a->zero_tail && !a->out_k) {
             for (int b = 0; b < a->B; ++b) {
                 int64_t sl = a->seq_lens[b];
                 if (sl <= 0) continue;
@@ -445,6 +495,15 @@ int oracle_norm_rope_append(const oracle_nra_args *a)
                        (size_t)(n * esz));
                 memset((char *)a->v_cache + (page * a->v_page_stride + (last + 1) * row_elems) * esz, 0,
                        (size_t)(n * esz));
+                if (a->kv_scale_mode) {
+                    /* the cleared rows' dynamic scales are zeroed too */
+                    int64_t ns = (int64_t)a->Hkv * (a->D / kv_group(a));
+                    int64_t first = (page * a->page_size + last + 1) * ns;
+                    for (int64_t i = 0; i < (a->page_size - 1 - last) * ns; ++i) {
+                        a->k_scale_out[first + i] = 0.0f;
+                        a->v_scale_out[first + i] = 0.0f;
+                    }
+                }
             }
         }
         return ORC_OK;
@@ -454,7 +513,7 @@ int oracle_norm_rope_append(const oracle_nra_args *a)
     for (int64_t t = 0; t < a->T; ++t) {
         if (position_out_of_table(a, t)) continue;
         int64_t pos = a->rot ? a->positions[t] : 0;
-        int64_t slot = a->slot_mapping[t];
+        int64_t slot = a->slot_mapping ? a->slot_mapping[t] : -1;
         int64_t page = -1, row = 0;
         if (slot >= 0 && slot < capacity) {
             page = slot / a->page_size;

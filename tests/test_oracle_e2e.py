@@ -19,14 +19,22 @@ import workloads as W
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
+def _copy(a):
+    return None if a is None else a.copy()
+
+
 def run_oracle(inp: W.NraInputs):
     out = {
         "qkv": inp.qkv.copy(),
         "k_cache": inp.k_cache0.copy(),
         "v_cache": inp.v_cache0.copy(),
         "q_out": None if inp.q_in_place else inp.q_out0.copy(),
-        "q_scale": None if inp.q_scale0 is None else inp.q_scale0.copy(),
-        "flags": None if inp.flags0 is None else inp.flags0.copy(),
+        "q_scale": _copy(inp.q_scale0),
+        "flags": _copy(inp.flags0),
+        "out_k": _copy(inp.out_k0),
+        "out_v": _copy(inp.out_v0),
+        "k_scale_out": _copy(inp.k_scale_out0),
+        "v_scale_out": _copy(inp.v_scale_out0),
     }
     oracle.norm_rope_append(inp, out)
     return out
@@ -520,3 +528,112 @@ def test_mla_static_fp8_q_rotates_only_the_rope_slice():
         for h in range(inp.H):
             o = oracle.rope(x[t, h, N:], W.ROPE_NEOX, c, s).astype(np.float32)
             assert np.array_equal(out["q_out"][t, h, N:], oracle.f64_to_e4m3(o.astype(np.float64)))
+
+
+
+# ----------------------------------------------------------------------------
+# K/V redirect and dynamic K/V scales
+# ----------------------------------------------------------------------------
+
+def _cell(inp, t):
+    b = int(np.searchsorted(inp.q_indptr, t, side="right") - 1)
+    ql = int(inp.q_indptr[b + 1] - inp.q_indptr[b])
+    L = int(inp.seq_lens[b]) - ql + (t - int(inp.q_indptr[b]))
+    return int(inp.page_table[b, L // inp.page_size]), L % inp.page_size
+
+
+@pytest.mark.parametrize("kv_fp8,mode", [(True, W.KV_SCALE_STATIC), (False, W.KV_SCALE_STATIC),
+                                         (True, W.KV_SCALE_TOKEN), (True, W.KV_SCALE_GROUP)])
+def test_redirected_kv_rows_equal_the_cache_rows_and_leave_the_caches_alone(kv_fp8, mode):
+    """FlashInfer "Contract" (caller-owned out_k / out_v) and its review (no
+    tail clear when K/V are redirected): row t of out_k / out_v holds what the
+    plain call writes at token t's cache cell, with the same scales; the
+    caches keep every byte; flags and Q are unchanged."""
+    kw = dict(kv_fp8=kv_fp8, k_scale=0.05, v_scale=0.07, kv_scale_mode=mode, kv_group_size=32,
+              q_mode=W.Q_FP8_DYNAMIC)
+    plain = _small(**kw)
+    red = _small(kv_redirect=True, **kw)
+    op, orr = run_oracle(plain), run_oracle(red)
+    assert np.array_equal(orr["k_cache"], red.k_cache0) and np.array_equal(orr["v_cache"], red.v_cache0)
+    assert np.array_equal(op["q_out"], orr["q_out"]) and np.array_equal(op["flags"], orr["flags"])
+    for t in range(plain.T):
+        page, row = _cell(plain, t)
+        assert np.array_equal(orr["out_k"][t], op["k_cache"][page, row])
+        assert np.array_equal(orr["out_v"][t], op["v_cache"][page, row])
+        if mode != W.KV_SCALE_STATIC:
+            crow = page * plain.page_size + row
+            assert np.array_equal(orr["k_scale_out"][t], op["k_scale_out"][crow])
+            assert np.array_equal(orr["v_scale_out"][t], op["v_scale_out"][crow])
+
+
+def test_token_kv_scales_closed_forms():
+    """Dynamic per-(token, kv head) K/V scales, s = max(amax, 1e-6) / 448 of
+    the encoded row: with no norm at position 0 (identity rotation) a K row
+    whose largest magnitude is 10 gets s = fp32(10/448) and that element
+    encodes to 448 (0x7E); an all-zero V row gets fp32(1e-6/448) and zero codes."""
+    inp = _small(kv_fp8=True, kv_scale_mode=W.KV_SCALE_TOKEN, norm=W.NORM_NONE, Hkv=1)
+    inp.positions = np.zeros(inp.T, np.int64)
+    qkv = inp.qkv.copy()
+    Hq, D = inp.Hq, inp.D
+    rng = np.random.default_rng(12)
+    qkv[:, Hq * D:(Hq + 1) * D] = W.to_bf16_bits(rng.uniform(-1, 1, size=(inp.T, D)))
+    qkv[0, Hq * D + 5] = W.to_bf16_bits(np.array([-10.0]))[0]
+    qkv[:, (Hq + 1) * D:(Hq + 2) * D] = 0
+    inp.qkv = qkv
+    out = run_oracle(inp)
+    page, row = _cell(inp, 0)
+    crow = page * inp.page_size + row
+    assert out["k_scale_out"][crow, 0, 0] == np.float32(10.0 / 448.0)
+    assert out["k_cache"][page, row, 0, 5] == 0xFE           # -448
+    assert out["v_scale_out"][crow, 0, 0] == np.float32(1e-6 / 448.0)
+    assert not out["v_cache"][page, row].any()
+    for t in range(inp.T):
+        page, row = _cell(inp, t)
+        crow = page * inp.page_size + row
+        x = W.bf16_bits_to_f32(inp.qkv[t, Hq * D:(Hq + 1) * D]).astype(np.float64)
+        s = out["k_scale_out"][crow, 0, 0]
+        assert s == np.float32(np.abs(x).max() / 448.0)
+        assert np.array_equal(out["k_cache"][page, row, 0], oracle.f64_to_e4m3(x / np.float64(s)))
+
+
+def test_group_kv_scales_follow_each_group_and_reduce_to_token_mode():
+    """Per-group scales (groups of 32 dims): group k of a V row with largest
+    magnitude 2^k gets s_k = fp32(2^k / 448); a group size equal to the head
+    dim gives exactly the per-token result."""
+    inp = _small(kv_fp8=True, kv_scale_mode=W.KV_SCALE_GROUP, kv_group_size=32, Hkv=1)
+    qkv = inp.qkv.copy()
+    Hq, D = inp.Hq, inp.D
+    rng = np.random.default_rng(13)
+    v = rng.uniform(-0.5, 0.5, size=(inp.T, D))
+    for k in range(D // 32):
+        v[:, 32 * k + 3] = 2.0 ** k
+    qkv[:, (Hq + 1) * D:(Hq + 2) * D] = W.to_bf16_bits(v)
+    inp.qkv = qkv
+    out = run_oracle(inp)
+    for t in range(inp.T):
+        page, row = _cell(inp, t)
+        crow = page * inp.page_size + row
+        for k in range(D // 32):
+            assert out["v_scale_out"][crow, 0, k] == np.float32(2.0 ** k / 448.0)
+            assert out["v_cache"][page, row, 0, 32 * k + 3] == 0x7E
+    tok = _small(kv_fp8=True, kv_scale_mode=W.KV_SCALE_TOKEN, Hkv=1)
+    grp = _small(kv_fp8=True, kv_scale_mode=W.KV_SCALE_GROUP, kv_group_size=D, Hkv=1)
+    ot, og = run_oracle(tok), run_oracle(grp)
+    for key in ("k_cache", "v_cache", "k_scale_out", "v_scale_out"):
+        assert np.array_equal(ot[key], og[key]), key
+
+
+def test_tail_clear_zeroes_the_dynamic_scales_of_cleared_rows():
+    inp = _small(kv_fp8=True, kv_scale_mode=W.KV_SCALE_TOKEN)
+    out = run_oracle(inp)
+    ps = inp.page_size
+    for b in range(inp.B):
+        sl = int(inp.seq_lens[b])
+        if sl <= 0:
+            continue
+        last = (sl - 1) % ps
+        page = int(inp.page_table[b, (sl - 1) // ps])
+        for r in range(last + 1, ps):
+            assert not out["k_scale_out"][page * ps + r].any()
+            assert not out["v_scale_out"][page * ps + r].any()
+            assert not out["k_cache"][page, r].any()

@@ -57,6 +57,7 @@ def sentinel_bytes(rng: np.random.Generator, nbytes: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 Q_BF16, Q_FP8_DYNAMIC, Q_FP8_STATIC = 0, 1, 2
+KV_SCALE_STATIC, KV_SCALE_TOKEN, KV_SCALE_GROUP = 0, 1, 2
 NORM_NONE, NORM_RMS, NORM_GEMMA = 0, 1, 2
 ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 ADDR_PAGED, ADDR_SLOT = 0, 1
@@ -107,6 +108,15 @@ class NraInputs:
     cache_seed: int = 0
     meta: dict = field(default_factory=dict)
     rotary_dim: int | None = None   # rotated dims per head (None: the whole head)
+    # K/V redirect to caller rows out_k / out_v [T, Hkv, D] (no cache write, no tail clear)
+    kv_redirect: bool = False
+    out_k0: np.ndarray | None = None
+    out_v0: np.ndarray | None = None
+    # FP8 K/V scales: KV_SCALE_STATIC, KV_SCALE_TOKEN (per token and kv head), KV_SCALE_GROUP
+    kv_scale_mode: int = 0
+    kv_group_size: int = 0
+    k_scale_out0: np.ndarray | None = None   # fp32 [cache rows or T, Hkv, D / group]
+    v_scale_out0: np.ndarray | None = None
 
     @property
     def R(self) -> int:
@@ -115,6 +125,10 @@ class NraInputs:
     @property
     def rot(self) -> int:
         return self.D if self.rotary_dim is None else self.rotary_dim
+
+    @property
+    def kv_group(self) -> int:
+        return self.kv_group_size if self.kv_scale_mode == KV_SCALE_GROUP else self.D
 
     @property
     def kv_elt(self) -> int:
@@ -166,7 +180,11 @@ class NraInputs:
                 sl = int(self.seq_lens[b])
                 if sl > 0:
                     tail_rows += self.page_size - 1 - (sl - 1) % self.page_size
+        if self.kv_redirect:
+            tail_rows = 0
+        ng = D // self.kv_group if self.kv_scale_mode else 0
         d = {
+            "kv_scales": (T + tail_rows) * 2 * Hkv * ng * 4,
             "qkv_read": T * self.R * D * 2,
             "norm_weights": (2 * D * 4) if self.norm != NORM_NONE else 0,
             "cos_sin": T * self.rot * 4,
@@ -185,7 +203,8 @@ def nra_case(*, name="custom", seed, q_lens, prior_lens, Hq, Hkv, D, page_size,
              cs_rows=None, kv_fp8=False, q_mode=Q_BF16, q_scale_padded=False, max_seqlen=0,
              upper_max=448.0, q_scale_inv=1.0, k_scale=1.0, v_scale=1.0, zero_tail=True,
              q_in_place=False, k_in_place=False, addressing=ADDR_PAGED, spare_pages=None,
-             maxp=None, host_caches=True, positions=None, rotary_dim=None) -> NraInputs:
+             maxp=None, host_caches=True, positions=None, rotary_dim=None, kv_redirect=False,
+             kv_scale_mode=KV_SCALE_STATIC, kv_group_size=0) -> NraInputs:
     """Draw one norm-rope-append call.
 
     Request b appends ``q_lens[b]`` tokens after ``prior_lens[b]`` cached
@@ -266,6 +285,16 @@ def nra_case(*, name="custom", seed, q_lens, prior_lens, Hq, Hkv, D, page_size,
             shape = (T, Hq)
         q_scale0 = sentinel_bytes(rng, int(np.prod(shape)) * 4).view(np.float32).reshape(shape)
     flags0 = np.full((B, Hkv), 0x5A5A5A5A, np.int32) if addressing == ADDR_PAGED else None
+    out_k0 = out_v0 = None
+    if kv_redirect:
+        out_k0 = sentinel_bytes(rng, T * Hkv * D * kv_elt).view(cache_dtype).reshape(T, Hkv, D)
+        out_v0 = sentinel_bytes(rng, T * Hkv * D * kv_elt).view(cache_dtype).reshape(T, Hkv, D)
+    k_scale_out0 = v_scale_out0 = None
+    if kv_scale_mode != KV_SCALE_STATIC:
+        g = kv_group_size if kv_scale_mode == KV_SCALE_GROUP else D
+        rows = T if kv_redirect else num_pages * page_size
+        k_scale_out0 = sentinel_bytes(rng, rows * Hkv * (D // g) * 4).view(np.float32).reshape(rows, Hkv, D // g)
+        v_scale_out0 = sentinel_bytes(rng, rows * Hkv * (D // g) * 4).view(np.float32).reshape(rows, Hkv, D // g)
     return NraInputs(
         name=name, T=T, Hq=Hq, Hkv=Hkv, D=D, B=B, qkv=qkv, qkv_row_stride=stride,
         norm=norm, eps=eps, q_norm_weight=qw.astype(np.float32), k_norm_weight=kw.astype(np.float32),
@@ -280,7 +309,9 @@ def nra_case(*, name="custom", seed, q_lens, prior_lens, Hq, Hkv, D, page_size,
         upper_max=upper_max, k_cache0=k_cache0, v_cache0=v_cache0, q_out0=q_out0,
         q_scale0=q_scale0, flags0=flags0, cache_seed=cache_seed,
         meta={"seed": seed, "q_lens": q_lens.tolist() if B <= 64 else None},
-        rotary_dim=rot,
+        rotary_dim=rot, kv_redirect=kv_redirect, out_k0=out_k0, out_v0=out_v0,
+        kv_scale_mode=kv_scale_mode, kv_group_size=kv_group_size if kv_scale_mode == KV_SCALE_GROUP else 0,
+        k_scale_out0=k_scale_out0, v_scale_out0=v_scale_out0,
     )
 
 
