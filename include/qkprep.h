@@ -80,6 +80,11 @@ typedef enum {
                                       /* row length P = round_up(max_seqlen, 128)             */
 } qkprep_qscale_layout;
 typedef enum { QKPREP_ADDR_PAGED = 0, QKPREP_ADDR_SLOT = 1 } qkprep_addressing;
+typedef enum {
+    QKPREP_KV_SCALE_STATIC = 0,    /* device scalars k_scale / v_scale */
+    QKPREP_KV_SCALE_TOKEN = 1,     /* dynamic, one per (token, kv head) */
+    QKPREP_KV_SCALE_GROUP = 2      /* dynamic, one per kv_group_size consecutive dims */
+} qkprep_kv_scale_mode;
 
 /*
  * qkprep_norm_rope_append -- Q/K RMSNorm + RoPE + (FP8) quantisation + paged
@@ -157,8 +162,8 @@ typedef struct qkprep_norm_rope_append_params {
     int32_t page_size;             /* >= 1 */
     int64_t k_page_stride;         /* elements between pages, >= page_size * Hkv * D, 16-B multiple */
     int64_t v_page_stride;
-    const float* k_scale;          /* device fp32 scalar (FP8 cache only) */
-    const float* v_scale;          /* device fp32 scalar (FP8 cache only) */
+    const float* k_scale;          /* device fp32 scalar (FP8 cache, static scales only) */
+    const float* v_scale;          /* device fp32 scalar (FP8 cache, static scales only) */
     int32_t zero_tail;             /* paged only; 1 in the pages' contract */
 
     void* q_out;                   /* [T][q_out_row_stride]: bf16 (Q_BF16) or E4M3 codes; may be
@@ -176,6 +181,31 @@ typedef struct qkprep_norm_rope_append_params {
     int64_t k_out_row_stride;      /* >= Hkv * D, multiple of 8 */
 
     int32_t* flags;                /* int32 [B][Hkv] (paged); may be NULL when B == 0 */
+
+    /* K/V redirect (FlashInfer PR "Contract": caller-owned out_k / out_v; its
+     * review: no tail clear when K/V are redirected).  With out_k and out_v
+     * set, the K and V rows of token t go to out_k[t][h][:] / out_v[t][h][:]
+     * (kv_dtype, same encoding as a cache row) instead of the caches; the
+     * caches are neither read nor written (they and the slot mapping may be
+     * NULL), zero_tail is ignored, and the paged metadata is validated as
+     * usual (flags). */
+    void* out_k;                   /* [T][out_kv_row_stride] of kv_dtype, 16-B aligned; NULL = no redirect */
+    void* out_v;                   /* set together with out_k */
+    int64_t out_kv_row_stride;     /* >= Hkv * D elements, 16-B multiple */
+
+    /* FP8 K/V scales (vLLM issue: static per-tensor, dynamic per-token and
+     * dynamic per-group quantisation).  Dynamic modes encode each group of g
+     * dims (g = D per token, else kv_group_size) as E4M3(x / s) with
+     * s = max(max |x| over the group, 1e-6) / 448 (x: K after norm + RoPE, V
+     * raw) and store s at k_scale_out / v_scale_out, fp32
+     * [num_pages * page_size][Hkv][D / g] indexed by the cache row
+     * page * page_size + row (or [T][Hkv][D / g] by token with out_k / out_v).
+     * A cleared tail row gets zero scales.  Needs the FP8 cache; GROUP needs
+     * kv_group_size a power of two in [8, D/2] (or D) and rotary_dim == D. */
+    int32_t kv_scale_mode;         /* qkprep_kv_scale_mode */
+    int32_t kv_group_size;
+    float* k_scale_out;
+    float* v_scale_out;
 } qkprep_norm_rope_append_params;
 
 /*

@@ -24,6 +24,7 @@ BF16, FP8_E4M3 = 0, 1
 NORM_NONE, NORM_RMS, NORM_GEMMA = 0, 1, 2
 ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 Q_BF16, Q_FP8_DYNAMIC, Q_FP8_STATIC = 0, 1, 2
+KV_SCALE_STATIC, KV_SCALE_TOKEN, KV_SCALE_GROUP = 0, 1, 2
 QSCALE_TOKEN_HEAD, QSCALE_REQ_HEAD_PADDED = 0, 1
 ADDR_PAGED, ADDR_SLOT = 0, 1
 
@@ -51,6 +52,8 @@ class NormRopeAppendParams(ctypes.Structure):
         ("q_scale_layout", _i32), ("max_seqlen", _i32), ("q_scale_inv", _vp), ("upper_max", _f32),
         ("k_out", _vp), ("k_out_row_stride", _i64),
         ("flags", _vp),
+        ("out_k", _vp), ("out_v", _vp), ("out_kv_row_stride", _i64),
+        ("kv_scale_mode", _i32), ("kv_group_size", _i32), ("k_scale_out", _vp), ("v_scale_out", _vp),
     ]
 
 
@@ -149,7 +152,9 @@ def norm_rope_append_params(*, qkv, num_q_heads, num_kv_heads, head_dim, cos_sin
                             q_scale=None, q_scale_layout=QSCALE_TOKEN_HEAD, max_seqlen=0, q_scale_inv=None,
                             upper_max=448.0, k_out=None, k_out_row_stride=None, flags=None,
                             num_tokens=None, qkv_row_stride=None, num_requests=None,
-                            rotary_dim=None) -> NormRopeAppendParams:
+                            rotary_dim=None, out_k=None, out_v=None, out_kv_row_stride=None,
+                            kv_scale_mode=KV_SCALE_STATIC, kv_group_size=0, k_scale_out=None,
+                            v_scale_out=None) -> NormRopeAppendParams:
     """Fill the params struct from tensors (shapes/strides read from them when not given)."""
     p = NormRopeAppendParams()
     p.num_tokens = qkv.shape[0] if num_tokens is None else num_tokens
@@ -171,10 +176,10 @@ def norm_rope_append_params(*, qkv, num_q_heads, num_kv_heads, head_dim, cos_sin
     p.slot_mapping = _ptr(slot_mapping)
     p.k_cache, p.v_cache = _ptr(k_cache), _ptr(v_cache)
     p.kv_dtype = kv_dtype
-    p.num_pages = k_cache.shape[0] if num_pages is None else num_pages
-    p.page_size = k_cache.shape[1] if page_size is None else page_size
-    p.k_page_stride = k_cache.stride(0) if k_page_stride is None else k_page_stride
-    p.v_page_stride = v_cache.stride(0) if v_page_stride is None else v_page_stride
+    p.num_pages = (k_cache.shape[0] if k_cache is not None else 0) if num_pages is None else num_pages
+    p.page_size = (k_cache.shape[1] if k_cache is not None else 0) if page_size is None else page_size
+    p.k_page_stride = (k_cache.stride(0) if k_cache is not None else 0) if k_page_stride is None else k_page_stride
+    p.v_page_stride = (v_cache.stride(0) if v_cache is not None else 0) if v_page_stride is None else v_page_stride
     p.k_scale, p.v_scale = _ptr(k_scale), _ptr(v_scale)
     p.zero_tail = zero_tail
     p.q_out = _ptr(q_out)
@@ -189,6 +194,11 @@ def norm_rope_append_params(*, qkv, num_q_heads, num_kv_heads, head_dim, cos_sin
     if k_out is not None:
         p.k_out_row_stride = k_out.stride(0) if k_out_row_stride is None else k_out_row_stride
     p.flags = _ptr(flags)
+    p.out_k, p.out_v = _ptr(out_k), _ptr(out_v)
+    if out_k is not None:
+        p.out_kv_row_stride = out_k.stride(0) if out_kv_row_stride is None else out_kv_row_stride
+    p.kv_scale_mode, p.kv_group_size = kv_scale_mode, kv_group_size
+    p.k_scale_out, p.v_scale_out = _ptr(k_scale_out), _ptr(v_scale_out)
     return p
 
 

@@ -192,6 +192,51 @@ __device__ __forceinline__ void store_fp8_lane(uint8_t* row, int gl, const LaneM
     }
 }
 
+// max over aligned groups of n lanes (n = 1, 2, 4, 8 or 16, the same for
+// the whole wave); every lane of a group receives the group's max
+__device__ __forceinline__ float subgroup_max(float v, int n) {
+    if (n >= 2) v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap1>(v));
+    if (n >= 4) v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap2>(v));
+    if (n >= 8) v = __builtin_fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
+    if (n >= 16) v = __builtin_fmaxf(v, dpp_f<kDppRowMirror>(v));
+    return v;
+}
+
+// E4M3 codes of a K or V head row with dynamic scales: one per group of
+// a.kv_group dims, s = max(amax, 1e-6) / 448, stored at sc[group].  With
+// a.kv_group == D the whole row shares one scale; smaller groups lie inside
+// one half of the lane split (whole-head rotary layout: the lane holds dims
+// [8 gl, 8 gl + 8) and [D/2 + 8 gl, D/2 + 8 gl + 8)) and span g/8 lanes.
+template <int D>
+__device__ __forceinline__ void kv_fp8_dynamic(const NraDevArgs& a, int gl, const float* x, float* sc, uint2& lo,
+                                               uint2& hi) {
+    constexpr int G = D / 16;
+    constexpr float kInv448 = 1.0f / 448.0f;
+    float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        m0 = __builtin_fmaxf(m0, __builtin_fabsf(x[i]));
+        m1 = __builtin_fmaxf(m1, __builtin_fabsf(x[8 + i]));
+    }
+    if (a.kv_group == D) {
+        const float s = __builtin_fmaxf(group_max<G>(__builtin_fmaxf(m0, m1)), 1e-6f) * kInv448;
+        const float mul = __builtin_amdgcn_rcpf(s);
+        if (gl == 0) sc[0] = s;
+        lo = pack8_fp8(x, mul);
+        hi = pack8_fp8(x + 8, mul);
+    } else {
+        const int n = a.kv_group >> 3;
+        const float s0 = __builtin_fmaxf(subgroup_max(m0, n), 1e-6f) * kInv448;
+        const float s1 = __builtin_fmaxf(subgroup_max(m1, n), 1e-6f) * kInv448;
+        if ((gl & (n - 1)) == 0) {
+            sc[(8 * gl) / a.kv_group] = s0;
+            sc[(D / 2 + 8 * gl) / a.kv_group] = s1;
+        }
+        lo = pack8_fp8(x, __builtin_amdgcn_rcpf(s0));
+        hi = pack8_fp8(x + 8, __builtin_amdgcn_rcpf(s1));
+    }
+}
+
 // Encodes and stores head row r of tile token ti (global token t) whose two
 // 16-byte vectors v0 / v1 (elements at lm.o0 / lm.o1) are in registers.
 // Q/K rows: RMSNorm (weights from LDS), RoPE on the rotated dims (cos/sin
@@ -200,6 +245,7 @@ __device__ __forceinline__ void store_fp8_lane(uint8_t* row, int gl, const LaneM
 struct RowConsts {
     float inv_k, inv_v, q_static, inv_um;
     int qs_hstride;
+    int kv_ng;       // dynamic K/V scales per head row (0: static scalars)
     float* s_qs;     // non-null: stage dynamic Q scales in LDS [token][head]
 };
 
@@ -207,20 +253,27 @@ template <int D, int QMODE, bool KVFP8>
 __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, int r, int gl, const LaneMap& lm,
                                             uint4 v0, uint4 v1, const float* s_w, const float* s_cs_row,
                                             const int64_t* s_koff, const int64_t* s_voff, const int64_t* s_qsoff,
-                                            const RowConsts& k) {
+                                            const int64_t* s_srow, const RowConsts& k) {
     constexpr int G = D / 16;
     typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
     if (r >= a.Hq + a.Hkv) {
         // V head: raw copy (bf16 cache) or x / v_scale (FP8 cache)
         const int64_t voff = s_voff[ti];
         if (voff < 0) return;
-        kv_t* row = reinterpret_cast<kv_t*>(a.v_cache) + voff + (r - a.Hq - a.Hkv) * D;
+        const int vh = r - a.Hq - a.Hkv;
+        kv_t* row = reinterpret_cast<kv_t*>(a.v_cache) + voff + vh * D;
         if constexpr (KVFP8) {
             float x[16];
             unpack8(v0, x);
             unpack8(v1, x + 8);
-            store_fp8_lane(reinterpret_cast<uint8_t*>(row), gl, lm, pack8_fp8(x, k.inv_v),
-                           pack8_fp8(x + 8, k.inv_v));
+            uint2 lo, hi;
+            if (k.kv_ng) {
+                kv_fp8_dynamic<D>(a, gl, x, a.v_scale_out + (s_srow[ti] * a.Hkv + vh) * k.kv_ng, lo, hi);
+            } else {
+                lo = pack8_fp8(x, k.inv_v);
+                hi = pack8_fp8(x + 8, k.inv_v);
+            }
+            store_fp8_lane(reinterpret_cast<uint8_t*>(row), gl, lm, lo, hi);
         } else {
             st16(row + lm.o0, v0);
             st16(row + lm.o1, v1);
@@ -312,8 +365,14 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
         if (koff >= 0) {
             kv_t* row = reinterpret_cast<kv_t*>(a.k_cache) + koff + kh * D;
             if constexpr (KVFP8) {
-                store_fp8_lane(reinterpret_cast<uint8_t*>(row), gl, lm, pack8_fp8(x, k.inv_k),
-                               pack8_fp8(x + 8, k.inv_k));
+                uint2 lo, hi;
+                if (k.kv_ng) {
+                    kv_fp8_dynamic<D>(a, gl, x, a.k_scale_out + (s_srow[ti] * a.Hkv + kh) * k.kv_ng, lo, hi);
+                } else {
+                    lo = pack8_fp8(x, k.inv_k);
+                    hi = pack8_fp8(x + 8, k.inv_k);
+                }
+                store_fp8_lane(reinterpret_cast<uint8_t*>(row), gl, lm, lo, hi);
             } else {
                 st16(row + lm.o0, pack8_bf16(x));
                 st16(row + lm.o1, pack8_bf16(x + 8));
@@ -356,6 +415,7 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     __shared__ int64_t s_koff[kMaxTokensPerTile];
     __shared__ int64_t s_voff[kMaxTokensPerTile];
     __shared__ int64_t s_qsoff[kMaxTokensPerTile];
+    __shared__ int64_t s_srow[kMaxTokensPerTile];    // cache row (page * page_size + row) or token, for K/V scales
     __shared__ int s_tail[kTailPrefetch];
     __shared__ int s_flag[4];
 
@@ -433,15 +493,22 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
             const int64_t p64 = a.rot > 0 ? a.positions[t] : 0;
             s_pos[tid] = (a.rot == 0 || (p64 >= 0 && p64 < a.cs_rows)) ? (int)p64 : -1;
             if (!a.paged) {
-                int64_t koff = -1, voff = -1;
-                const int64_t slot = a.slot_mapping[t];
-                if (slot >= 0 && slot < (int64_t)a.num_pages * a.page_size) {
-                    const int64_t page = slot / a.page_size, row = slot % a.page_size;
-                    koff = page * a.k_page_stride + row * row_elems;
-                    voff = page * a.v_page_stride + row * row_elems;
+                int64_t koff = -1, voff = -1, srow = -1;
+                if (a.redirect) {
+                    koff = voff = (int64_t)t * a.kv_out_stride;
+                    srow = t;
+                } else {
+                    const int64_t slot = a.slot_mapping[t];
+                    if (slot >= 0 && slot < (int64_t)a.num_pages * a.page_size) {
+                        const int64_t page = slot / a.page_size, row = slot % a.page_size;
+                        koff = page * a.k_page_stride + row * row_elems;
+                        voff = page * a.v_page_stride + row * row_elems;
+                        srow = slot;
+                    }
                 }
                 s_koff[tid] = koff;
                 s_voff[tid] = voff;
+                s_srow[tid] = srow;
                 s_qsoff[tid] = (int64_t)t * a.Hq;
             }
         }
@@ -457,11 +524,17 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
             const int ql = s_indptr[b + 1] - beg;
             const int j = t - beg;
             const int L = s_seqlen[b] - ql + j;
-            const int pidx = min(max(L / a.page_size, 0), a.maxp - 1);
-            const int64_t page = a.page_table[(int64_t)b * a.maxp + pidx];
-            const int64_t row = L % a.page_size;
-            s_koff[tid] = page * a.k_page_stride + row * row_elems;
-            s_voff[tid] = page * a.v_page_stride + row * row_elems;
+            if (a.redirect) {
+                s_koff[tid] = s_voff[tid] = (int64_t)t * a.kv_out_stride;
+                s_srow[tid] = t;
+            } else {
+                const int pidx = min(max(L / a.page_size, 0), a.maxp - 1);
+                const int64_t page = a.page_table[(int64_t)b * a.maxp + pidx];
+                const int64_t row = L % a.page_size;
+                s_koff[tid] = page * a.k_page_stride + row * row_elems;
+                s_voff[tid] = page * a.v_page_stride + row * row_elems;
+                s_srow[tid] = page * a.page_size + row;
+            }
             s_qsoff[tid] = a.q_scale_padded ? (int64_t)b * a.Hq * a.q_scale_P + j : (int64_t)t * a.Hq;
         }
         // table rows hold R floats (staged at a stride of D)
@@ -488,8 +561,9 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
 
     // device scalars of the call, loaded with the first round of metadata
     RowConsts kc;
-    kc.inv_k = KVFP8 ? 1.0f / *a.k_scale : 1.0f;
-    kc.inv_v = KVFP8 ? 1.0f / *a.v_scale : 1.0f;
+    kc.inv_k = (KVFP8 && a.kv_group == 0) ? 1.0f / *a.k_scale : 1.0f;
+    kc.inv_v = (KVFP8 && a.kv_group == 0) ? 1.0f / *a.v_scale : 1.0f;
+    kc.kv_ng = a.kv_group ? D / a.kv_group : 0;
     kc.q_static = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
     kc.inv_um = (QMODE == 1) ? 1.0f / a.upper_max : 1.0f;
     kc.qs_hstride = a.q_scale_padded ? (int)a.q_scale_P : 1;
@@ -544,7 +618,7 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
                 const int ti = pr.t - t_first;
                 if (r < a.R && s_pos[ti] >= 0)
                     process_row<D, QMODE, KVFP8>(a, pr.t, ti, r, gl, lm, buf[u][0], buf[u][1], s_w,
-                                                 s_cs + ti * D, s_koff, s_voff, s_qsoff, kc);
+                                                 s_cs + ti * D, s_koff, s_voff, s_qsoff, s_srow, kc);
                 pr.advance(CPT);
             }
         }
@@ -571,6 +645,16 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
         for (int64_t i = tid; i < nvec; i += kBlockThreads) {
             st16(kb + 16 * i, z);
             st16(vb + 16 * i, z);
+        }
+        if (kc.kv_ng) {
+            // the cleared rows' dynamic scales
+            const int64_t ns = (int64_t)a.Hkv * kc.kv_ng;
+            const int64_t first = (page * a.page_size + last + 1) * ns;
+            const int64_t cnt = (int64_t)(a.page_size - 1 - last) * ns;
+            for (int64_t i = tid; i < cnt; i += kBlockThreads) {
+                a.k_scale_out[first + i] = 0.0f;
+                a.v_scale_out[first + i] = 0.0f;
+            }
         }
     }
 

@@ -50,6 +50,21 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
         p->q_scale_layout < 0 || p->q_scale_layout > 1)
         return QKPREP_E_RANGE;
     if (p->page_size <= 0) return QKPREP_E_RANGE;
+    const bool redirect = p->out_k != nullptr || p->out_v != nullptr;
+    if (redirect && (!p->out_k || !p->out_v)) return QKPREP_E_NULL;
+    if (p->kv_scale_mode < 0 || p->kv_scale_mode > 2) return QKPREP_E_RANGE;
+    const bool kv_dyn = p->kv_scale_mode != QKPREP_KV_SCALE_STATIC;
+    int kv_group = 0;
+    if (kv_dyn) {
+        if (p->kv_dtype != QKPREP_FP8_E4M3) return QKPREP_E_UNSUPPORTED;
+        kv_group = D;
+        if (p->kv_scale_mode == QKPREP_KV_SCALE_GROUP) {
+            const int g = p->kv_group_size;
+            if (g < 8 || (g & (g - 1)) || (g > D / 2 && g != D)) return QKPREP_E_UNSUPPORTED;
+            if (g != D && rot != D) return QKPREP_E_UNSUPPORTED;
+            kv_group = g;
+        }
+    }
     if (p->norm != 0 && !(p->eps > 0.0f && isfinite(p->eps))) return QKPREP_E_RANGE;
     if (p->q_mode == QKPREP_Q_FP8_DYNAMIC && !(p->upper_max > 0.0f && p->upper_max <= 448.0f))
         return QKPREP_E_RANGE;
@@ -71,14 +86,15 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     const int kv_elt = p->kv_dtype == QKPREP_FP8_E4M3 ? 1 : 2;
     const int q_elt = p->q_mode == QKPREP_Q_BF16 ? 2 : 1;
     // pointers
-    if (!p->k_cache || !p->v_cache) return QKPREP_E_NULL;
-    if (p->kv_dtype == QKPREP_FP8_E4M3 && (!p->k_scale || !p->v_scale)) return QKPREP_E_NULL;
+    if (!redirect && (!p->k_cache || !p->v_cache)) return QKPREP_E_NULL;
+    if (p->kv_dtype == QKPREP_FP8_E4M3 && !kv_dyn && (!p->k_scale || !p->v_scale)) return QKPREP_E_NULL;
+    if (kv_dyn && (!p->k_scale_out || !p->v_scale_out)) return QKPREP_E_NULL;
     if (paged && (!p->q_indptr || !p->seq_lens || !p->page_table || !p->flags)) return QKPREP_E_NULL;
     if (T > 0) {
         if (!p->qkv || !p->q_out) return QKPREP_E_NULL;
         if (rot > 0 && (!p->cos_sin_cache || !p->positions)) return QKPREP_E_NULL;
         if (p->norm != 0 && (!p->q_norm_weight || !p->k_norm_weight)) return QKPREP_E_NULL;
-        if (!paged && !p->slot_mapping) return QKPREP_E_NULL;
+        if (!paged && !redirect && !p->slot_mapping) return QKPREP_E_NULL;
         if (p->q_mode == QKPREP_Q_FP8_DYNAMIC && !p->q_scale) return QKPREP_E_NULL;
         if (p->q_mode == QKPREP_Q_FP8_STATIC && !p->q_scale_inv) return QKPREP_E_NULL;
     }
@@ -86,11 +102,17 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     if (p->num_pages < 1) return QKPREP_E_SHAPE;
     if (paged && p->max_pages_per_request < 1) return QKPREP_E_SHAPE;
     const int64_t row_elems = (int64_t)Hkv * D;
-    if (p->k_page_stride < (int64_t)p->page_size * row_elems ||
-        p->v_page_stride < (int64_t)p->page_size * row_elems)
-        return QKPREP_E_SHAPE;
-    if ((p->k_page_stride * kv_elt) % 16 || (p->v_page_stride * kv_elt) % 16) return QKPREP_E_ALIGN;
-    if (!aligned16(p->k_cache) || !aligned16(p->v_cache)) return QKPREP_E_ALIGN;
+    if (redirect) {
+        if (p->out_kv_row_stride < row_elems) return QKPREP_E_SHAPE;
+        if ((p->out_kv_row_stride * kv_elt) % 16 || !aligned16(p->out_k) || !aligned16(p->out_v))
+            return QKPREP_E_ALIGN;
+    } else {
+        if (p->k_page_stride < (int64_t)p->page_size * row_elems ||
+            p->v_page_stride < (int64_t)p->page_size * row_elems)
+            return QKPREP_E_SHAPE;
+        if ((p->k_page_stride * kv_elt) % 16 || (p->v_page_stride * kv_elt) % 16) return QKPREP_E_ALIGN;
+        if (!aligned16(p->k_cache) || !aligned16(p->v_cache)) return QKPREP_E_ALIGN;
+    }
     if (T > 0) {
         if (p->qkv_row_stride < (int64_t)R * D) return QKPREP_E_SHAPE;
         if (p->qkv_row_stride % 8) return QKPREP_E_ALIGN;
@@ -123,11 +145,16 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     a.q_indptr = p->q_indptr; a.seq_lens = p->seq_lens; a.page_table = p->page_table;
     a.maxp = p->max_pages_per_request;
     a.slot_mapping = p->slot_mapping;
-    a.k_cache = p->k_cache; a.v_cache = p->v_cache;
+    a.k_cache = redirect ? p->out_k : p->k_cache;
+    a.v_cache = redirect ? p->out_v : p->v_cache;
+    a.redirect = redirect ? 1 : 0;
+    a.kv_out_stride = redirect ? p->out_kv_row_stride : 0;
+    a.kv_group = kv_group;
+    a.k_scale_out = p->k_scale_out; a.v_scale_out = p->v_scale_out;
     a.num_pages = p->num_pages; a.page_size = p->page_size;
     a.k_page_stride = p->k_page_stride; a.v_page_stride = p->v_page_stride;
     a.k_scale = p->k_scale; a.v_scale = p->v_scale;
-    a.zero_tail = paged && p->zero_tail ? 1 : 0;
+    a.zero_tail = paged && !redirect && p->zero_tail ? 1 : 0;
     a.q_out = p->q_out; a.q_out_stride = p->q_out_row_stride;
     a.q_scale = p->q_scale;
     a.q_scale_padded = padded ? 1 : 0;

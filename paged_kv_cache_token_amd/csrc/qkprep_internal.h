@@ -65,6 +65,13 @@ struct NraDevArgs {
     int32_t tokens_per_tile;            // most tokens staged in LDS at once
     int32_t chunks_per_token;           // ceil(R / head rows per wave)
     int64_t total_items;                // T * chunks_per_token
+    // K/V redirect: k_cache / v_cache point at out_k / out_v, rows by token
+    int32_t redirect;
+    int64_t kv_out_stride;              // elements between token rows (redirect)
+    // dynamic FP8 K/V scales: dims per scale (0 = static scalars)
+    int32_t kv_group;
+    float* k_scale_out;
+    float* v_scale_out;
     int32_t interleave;                 // items per round-robin span, 0 = one range per workgroup
     int32_t grid;                       // workgroups launched (set by the launcher)
 };

@@ -106,6 +106,14 @@ class DeviceNra:
         self.k_scale = _scalar(inp.k_scale)
         self.v_scale = _scalar(inp.v_scale)
         self.q_scale_inv = _scalar(inp.q_scale_inv)
+        self.out_k = self.out_v = self.k_scale_out = self.v_scale_out = None
+        if inp.kv_redirect:
+            self.out_k = Guarded(inp.out_k0.nbytes, cdt, inp.out_k0.shape, init=inp.out_k0)
+            self.out_v = Guarded(inp.out_v0.nbytes, cdt, inp.out_v0.shape, init=inp.out_v0)
+        if inp.kv_scale_mode:
+            sh = inp.k_scale_out0.shape
+            self.k_scale_out = Guarded(inp.k_scale_out0.nbytes, torch.float32, sh, init=inp.k_scale_out0)
+            self.v_scale_out = Guarded(inp.v_scale_out0.nbytes, torch.float32, sh, init=inp.v_scale_out0)
 
     def kwargs(self) -> dict:
         inp = self.inp
@@ -132,13 +140,19 @@ class DeviceNra:
             max_seqlen=inp.max_seqlen, q_scale_inv=self.q_scale_inv, upper_max=inp.upper_max,
             k_out=k_out, k_out_row_stride=inp.qkv_row_stride,
             flags=None if self.flags is None else self.flags.t, rotary_dim=inp.rot,
+            out_k=None if self.out_k is None else self.out_k.t,
+            out_v=None if self.out_v is None else self.out_v.t,
+            kv_scale_mode=inp.kv_scale_mode, kv_group_size=inp.kv_group_size,
+            k_scale_out=None if self.k_scale_out is None else self.k_scale_out.t,
+            v_scale_out=None if self.v_scale_out is None else self.v_scale_out.t,
         )
 
     def run(self, stream=None):
         qp.qkprep_norm_rope_append(stream=stream, **self.kwargs())
 
     def guards_intact(self) -> bool:
-        bufs = [self.qkv, self.k_cache, self.v_cache, self.q_out, self.q_scale, self.flags]
+        bufs = [self.qkv, self.k_cache, self.v_cache, self.q_out, self.q_scale, self.flags, self.out_k,
+                self.out_v, self.k_scale_out, self.v_scale_out]
         return all(b.guards_intact() for b in bufs if b is not None)
 
     def host_outputs(self, pages: np.ndarray | None = None) -> dict:
@@ -159,6 +173,12 @@ class DeviceNra:
             "q_scale": None if self.q_scale is None else self.q_scale.t.cpu().numpy(),
             "flags": None if self.flags is None else self.flags.t.cpu().numpy(),
         }
+        for name in ("out_k", "out_v"):
+            g = getattr(self, name)
+            out[name] = None if g is None else g.t.cpu().numpy().view(cdt)
+        for name in ("k_scale_out", "v_scale_out"):
+            g = getattr(self, name)
+            out[name] = None if g is None else g.t.cpu().numpy()
         return out
 
 
@@ -171,6 +191,9 @@ def oracle_outputs(inp: W.NraInputs) -> dict:
         "q_scale": None if inp.q_scale0 is None else inp.q_scale0.copy(),
         "flags": None if inp.flags0 is None else inp.flags0.copy(),
     }
+    for name in ("out_k0", "out_v0", "k_scale_out0", "v_scale_out0"):
+        a = getattr(inp, name)
+        out[name[:-1]] = None if a is None else a.copy()
     oracle.norm_rope_append(inp, out)
     return out
 
@@ -252,6 +275,8 @@ def written_cells(inp: W.NraInputs, pages_index=None):
     """(token, page, row) of every token the call appends (valid position and
     slot); page numbers relabelled through `pages_index` when given."""
     out = []
+    if inp.kv_redirect:
+        return out
     rows = inp.cos_sin.shape[0]
     for t in range(inp.T):
         pos = int(inp.positions[t])
@@ -329,16 +354,36 @@ def compare_nra(inp: W.NraInputs, gpu: dict, ref: dict) -> dict:
     check_exact(gq, rq, "qkv (V, padding and unwritten columns)")
     # q_scale
     if ref["q_scale"] is not None:
-        sg = gpu["q_scale"].reshape(-1)
-        sr = ref["q_scale"].reshape(-1)
-        s0 = inp.q_scale0.reshape(-1)
-        written = sr.view(np.uint32) != s0.view(np.uint32)
-        if written.any():
-            rel = np.abs(sg[written].astype(np.float64) - sr[written]) / np.abs(sr[written].astype(np.float64))
-            stats["q_scale"] = {"n": int(written.sum()), "max_rel": float(rel.max())}
-            assert rel.max() <= 1e-5, f"q_scale relative error {rel.max()}"
-        check_exact(sg[~written], sr[~written], "q_scale entries not written")
+        check_scales(gpu["q_scale"], ref["q_scale"], inp.q_scale0, "q_scale", stats)
+    # redirected K/V rows
+    if inp.kv_redirect:
+        for name in ("out_k", "out_v"):
+            g, r = gpu[name], ref[name]
+            if live.any():
+                if inp.kv_fp8:
+                    check_e4m3(g[live], r[live], name, stats)
+                elif name == "out_k":
+                    check_bf16(g[live], r[live], name, stats)
+                else:
+                    check_exact(g[live], r[live], "out_v (bf16 copy)")
+            check_exact(g[~live], r[~live], f"{name} rows not written")
+    if inp.kv_scale_mode:
+        check_scales(gpu["k_scale_out"], ref["k_scale_out"], inp.k_scale_out0, "k_scale_out", stats)
+        check_scales(gpu["v_scale_out"], ref["v_scale_out"], inp.v_scale_out0, "v_scale_out", stats)
     return stats
+
+
+def check_scales(got: np.ndarray, ref: np.ndarray, before: np.ndarray, what: str, stats: dict):
+    """fp32 scales: entries the oracle wrote within relative 1e-5 (zeros of
+    cleared rows exactly), every other entry byte-identical."""
+    g, r, b = got.reshape(-1), ref.reshape(-1), before.reshape(-1)
+    written = r.view(np.uint32) != b.view(np.uint32)
+    nz = written & (r != 0)
+    if nz.any():
+        rel = np.abs(g[nz].astype(np.float64) - r[nz]) / np.abs(r[nz].astype(np.float64))
+        stats[what] = {"n": int(nz.sum()), "max_rel": float(rel.max())}
+        assert rel.max() <= 1e-5, f"{what} relative error {rel.max()}"
+    check_exact(g[~nz], r[~nz], f"{what} entries not written or zeroed")
 
 
 # ----------------------------------------------------------------------------

@@ -105,6 +105,22 @@ def _status(p):
     (dict(k_page_stride=100), 2),
     (dict(addressing=1, q_mode=1, q_scale=0xD000, q_scale_layout=1, max_seqlen=8), 3),
     (dict(q_mode=1, q_scale=0xD000, q_scale_layout=1, max_seqlen=0), 5),
+    # K/V redirect and dynamic K/V scales
+    (dict(out_k=0xE000), 1),
+    (dict(out_v=0xE000), 1),
+    (dict(out_k=0xE000, out_v=0xF000, out_kv_row_stride=64), 2),
+    (dict(out_k=0xE000, out_v=0xF000, out_kv_row_stride=132), 4),
+    (dict(out_k=0xE008, out_v=0xF000, out_kv_row_stride=128), 4),
+    (dict(kv_scale_mode=3), 5),
+    (dict(kv_scale_mode=-1), 5),
+    (dict(kv_scale_mode=1, k_scale_out=0x10000, v_scale_out=0x11000), 3),            # bf16 cache
+    (dict(kv_dtype=1, kv_scale_mode=1, k_scale_out=None, v_scale_out=0x11000), 1),
+    (dict(kv_dtype=1, kv_scale_mode=2, kv_group_size=24, k_scale_out=0x10000, v_scale_out=0x11000), 3),
+    (dict(kv_dtype=1, kv_scale_mode=2, kv_group_size=4, k_scale_out=0x10000, v_scale_out=0x11000), 3),
+    (dict(kv_dtype=1, kv_scale_mode=2, kv_group_size=256, k_scale_out=0x10000, v_scale_out=0x11000), 3),
+    (dict(kv_dtype=1, kv_scale_mode=2, kv_group_size=32, rotary_dim=64, k_scale_out=0x10000,
+          v_scale_out=0x11000), 3),
+    (dict(kv_dtype=1, k_scale=None, v_scale=None), 1),
 ])
 def test_host_checks_reject_before_launch(over, expect):
     assert _status(_params(**over)) == expect

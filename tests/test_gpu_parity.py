@@ -141,6 +141,50 @@ def test_partial_rotary(D, R, arm):
     run_and_compare(inp)
 
 
+# K/V redirect to caller rows (caches untouched, no tail clear) and dynamic
+# FP8 K/V scales per (token, kv head) or per group of dims
+@pytest.mark.parametrize("addressing", [W.ADDR_PAGED, W.ADDR_SLOT])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp8_token", "fp8_group32"])
+def test_kv_redirect(addressing, kv):
+    q, prior = _ragged(91 + addressing, B=5, max_q=40, max_prior=200)
+    mode = {"bf16": 0, "fp8": 0, "fp8_token": W.KV_SCALE_TOKEN, "fp8_group32": W.KV_SCALE_GROUP}[kv]
+    inp = W.nra_case(seed=91, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=16,
+                     addressing=addressing, kv_fp8=kv != "bf16", k_scale=0.05, v_scale=0.05,
+                     q_mode=W.Q_FP8_DYNAMIC, kv_redirect=True, kv_scale_mode=mode, kv_group_size=32)
+    inp.positions = inp.positions.copy()
+    inp.positions[2] = -3
+    run_and_compare(inp)
+
+
+@pytest.mark.parametrize("D,mode,g", [(128, W.KV_SCALE_TOKEN, 0), (128, W.KV_SCALE_GROUP, 8),
+                                      (128, W.KV_SCALE_GROUP, 16), (128, W.KV_SCALE_GROUP, 32),
+                                      (128, W.KV_SCALE_GROUP, 64), (128, W.KV_SCALE_GROUP, 128),
+                                      (256, W.KV_SCALE_GROUP, 128), (256, W.KV_SCALE_TOKEN, 0),
+                                      (64, W.KV_SCALE_GROUP, 32), (64, W.KV_SCALE_TOKEN, 0)])
+@pytest.mark.parametrize("addressing", [W.ADDR_PAGED, W.ADDR_SLOT])
+def test_dynamic_kv_scales(D, mode, g, addressing):
+    q, prior = _ragged(D + g + addressing, B=6, max_q=35, max_prior=150)
+    inp = W.nra_case(seed=D + g, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=D, page_size=16,
+                     addressing=addressing, kv_fp8=True, kv_scale_mode=mode, kv_group_size=g,
+                     q_mode=W.Q_FP8_STATIC, q_scale_inv=2.0, norm=W.NORM_GEMMA, qkv_sigma=3.0)
+    run_and_compare(inp)
+
+
+@pytest.mark.parametrize("R", [64, 0])
+def test_token_kv_scales_with_partial_rotary(R):
+    q, prior = _ragged(R + 5, B=4, max_q=30, max_prior=100)
+    inp = W.nra_case(seed=R + 5, q_lens=q, prior_lens=prior, Hq=4, Hkv=4, D=128, page_size=8,
+                     rotary_dim=R, kv_fp8=True, kv_scale_mode=W.KV_SCALE_TOKEN)
+    run_and_compare(inp)
+
+
+def test_c3_with_per_token_kv_scales():
+    """The ragged 15k-token FP8 prefill with dynamic per-(token, kv head)
+    K/V scales instead of the static ones (page-64 cache, tails cleared)."""
+    inp = W.c3_prefill_fp8(kv_scale_mode=W.KV_SCALE_TOKEN)
+    print(run_and_compare(inp), flush=True)
+
+
 def test_head_dim_64_gqa_8_to_1():
     """64 Q heads over 8 KV heads of 64 dims (the GPT-OSS row of the vLLM
     issue's model table), FP8 Q with padded scales and E4M3 caches."""
