@@ -19,6 +19,7 @@ launches timed one at a time after a clean 512 MiB read flush of L2 and the
 256 MB Infinity Cache; and the CPU oracle timed on the host on the same step.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+       python bench.py --suite      (every configuration and variant, one by one)
 """
 from __future__ import annotations
 
@@ -53,7 +54,87 @@ def parse():
                     help="time one workload alone (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB copy (counter calibration) and exit")
+    ap.add_argument("--suite", action="store_true",
+                    help="time every workload (the five configurations and the variant rows) one by one "
+                         "and print one JSON object; no headline line")
+    ap.add_argument("--suite-only", default=None, help="comma-separated subset of the suite's workloads")
     return ap.parse_args()
+
+
+def suite_workloads():
+    """Name -> (constructor, kind) of every timed workload: the five
+    configurations, then the variants (partial rotary, 64-dim heads, MLA
+    with E4M3 Q, dynamic K/V scales, K/V redirect) at the prefill and MLA
+    shapes."""
+    import workloads as W
+    return {
+        "c1_tiny_decode": (W.c1_tiny_decode, "nra"),
+        "c2_decode_b256": (W.c2_decode_b256, "nra"),
+        "c3_prefill_fp8": (W.c3_prefill_fp8, "nra"),
+        "c4_strided_d256": (W.c4_strided_d256, "nra"),
+        "c5_mla": (W.c5_mla, "mla"),
+        "prefill_d64_gqa_64_8": (lambda: W.c3_prefill_fp8(D=64, name="prefill_d64"), "nra"),
+        "prefill_rotary_64_of_128": (lambda: W.c3_prefill_fp8(rotary_dim=64, name="prefill_r64"), "nra"),
+        "prefill_nope_layer": (lambda: W.c3_prefill_fp8(rotary_dim=0, name="prefill_r0"), "nra"),
+        "c5_mla_q_fp8_dynamic": (lambda: W.c5_mla(q_mode=W.Q_FP8_DYNAMIC), "mla"),
+        "c5_mla_q_fp8_static": (lambda: W.c5_mla(q_mode=W.Q_FP8_STATIC), "mla"),
+        "prefill_kv_token_scales": (lambda: W.c3_prefill_fp8(kv_scale_mode=W.KV_SCALE_TOKEN), "nra"),
+        "prefill_kv_group64_scales": (lambda: W.c3_prefill_fp8(kv_scale_mode=W.KV_SCALE_GROUP,
+                                                               kv_group_size=64), "nra"),
+        "prefill_kv_redirect": (lambda: W.c3_prefill_fp8(kv_redirect=True), "nra"),
+        "decode_b256_kv_redirect": (lambda: W.c2_decode_b256(kv_redirect=True), "nra"),
+    }
+
+
+def run_suite(args, dev):
+    """Each workload alone: the average of 20 back-to-back launches (events
+    on the launch stream around each) and the median of 15 launches after a
+    clean 512 MiB read flush."""
+    import torch
+    table = {}
+    names = list(suite_workloads())
+    if args.suite_only:
+        names = [n for n in args.suite_only.split(",") if n]
+    stream = torch.cuda.current_stream()
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    for name in names:
+        make, kind = suite_workloads()[name]
+        log(f"suite: {name}")
+        inp = make()
+        c = MlaCall(inp, dev) if kind == "mla" else Call(inp, dev)
+        for _ in range(3):
+            c.launch()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+        ev[0].record(stream)
+        for k in range(20):
+            c.launch()
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        warm = [ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(20)]
+        cold = []
+        for _ in range(15):
+            flush.sum()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            c.launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1) * 1e3)
+        cold.sort()
+        avg = sum(warm) / len(warm)
+        med = cold[len(cold) // 2]
+        table[name] = {"tokens": inp.T, "algorithmic_bytes": c.bytes, "avg_us": round(avg, 2),
+                       "clean_cache_median_us": round(med, 2),
+                       "GBps": round(c.bytes / (avg * 1e-6) / 1e9, 1),
+                       "clean_cache_GBps": round(c.bytes / (med * 1e-6) / 1e9, 1),
+                       "clean_cache_pct_of_peak": round(100 * c.bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                       "Mtok_per_s_clean": round(inp.T / med, 2)}
+        log(f"  {table[name]}")
+        del c
+        torch.cuda.empty_cache()
+    print(json.dumps({"suite": table, "peak_GBps": HBM_PEAK_GBS}), flush=True)
 
 
 class Call:
@@ -87,6 +168,14 @@ class Call:
                                                                   (inp.qkv_row_stride, 1))
         self.q_scale = None if inp.q_scale0 is None else up(inp.q_scale0, torch.float32)
         self.flags = up(inp.flags0, torch.int32)
+        redirect = {}
+        if inp.kv_redirect:
+            redirect = dict(out_k=up(inp.out_k0, cdt), out_v=up(inp.out_v0, cdt))
+        scales = {}
+        if inp.kv_scale_mode:
+            scales = dict(k_scale_out=up(inp.k_scale_out0, torch.float32),
+                          v_scale_out=up(inp.v_scale_out0, torch.float32))
+        self.extra = dict(redirect, **scales)
         sc = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)  # noqa: E731
         self.kw = dict(
             qkv=self.qkv, num_q_heads=inp.Hq, num_kv_heads=inp.Hkv, head_dim=inp.D, norm=inp.norm,
@@ -101,7 +190,8 @@ class Call:
             q_scale_inv=sc(inp.q_scale_inv), num_tokens=inp.T,
             q_scale=self.q_scale,
             q_scale_layout=qp.QSCALE_REQ_HEAD_PADDED if inp.q_scale_padded else qp.QSCALE_TOKEN_HEAD,
-            max_seqlen=inp.max_seqlen, upper_max=inp.upper_max, flags=self.flags)
+            max_seqlen=inp.max_seqlen, upper_max=inp.upper_max, flags=self.flags, rotary_dim=inp.rot,
+            kv_scale_mode=inp.kv_scale_mode, kv_group_size=inp.kv_group_size, **self.extra)
         self.params = qp.norm_rope_append_params(**self.kw)
         self.params.struct_size = ctypes.sizeof(self.params)
         self._ref = ctypes.byref(self.params)
@@ -245,6 +335,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_calibration:
         copy_calibration(dev)
+        return
+    if args.suite:
+        run_suite(args, dev)
         return
 
     log("generating decode B=256")

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import paged_kv_cache_token_amd as qp
 import workloads as W
 from tests import gpu_harness as H
 
@@ -247,6 +248,28 @@ def test_long_call_with_slot_addressing():
     inp.positions = inp.positions.copy()
     inp.positions[[3, 5000]] = [-1, inp.cos_sin.shape[0] + 2]
     run_and_compare(inp)
+
+
+def test_decode_mrope_positions_use_the_first_axis():
+    """Decode with multimodal RoPE (SGLang PR, Qwen3 dispatch: decode mRoPE
+    positions repeat one position on all three axes, so the first axis is
+    exact): passing row 0 of a [3, T] int64 positions tensor gives the same
+    bytes as the 1-D positions."""
+    inp = W.nra_case(seed=33, q_lens=np.ones(48, np.int64), prior_lens=np.arange(48) * 37 + 5, Hq=16,
+                     Hkv=2, D=128, page_size=16, q_mode=W.Q_FP8_DYNAMIC, kv_fp8=True, k_scale=0.05,
+                     v_scale=0.05)
+    plain = H.DeviceNra(inp)
+    plain.run()
+    mrope = H.DeviceNra(inp)
+    pos3 = plain.positions.unsqueeze(0).repeat(3, 1).contiguous()
+    kw = mrope.kwargs()
+    kw["positions"] = pos3[0]
+    qp.qkprep_norm_rope_append(**kw)
+    torch.cuda.synchronize()
+    a, b = plain.host_outputs(), mrope.host_outputs()
+    for k in ("q_out", "q_scale", "k_cache", "v_cache", "flags"):
+        assert np.array_equal(a[k], b[k]), k
+    H.compare_nra(inp, b, H.oracle_outputs(inp))
 
 
 def test_out_of_range_positions_suppress_tokens():
