@@ -17,7 +17,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libqkprep.so")
-SOURCES = ["qkprep_api.hip", "nra_kernel.hip", "mla_kernel.hip"]
+# (source, object name, extra flags): the norm-rope-append kernel is built
+# once per head dim so that its instances compile in parallel
+SOURCES = [
+    ("qkprep_api.hip", "qkprep_api", []),
+    ("nra_kernel.hip", "nra_d64", ["-DQKPREP_NRA_HEAD_DIM=64"]),
+    ("nra_kernel.hip", "nra_d128", ["-DQKPREP_NRA_HEAD_DIM=128"]),
+    ("nra_kernel.hip", "nra_d256", ["-DQKPREP_NRA_HEAD_DIM=256"]),
+    ("mla_kernel.hip", "mla_kernel", []),
+]
 ARCH = "gfx950"
 
 
@@ -41,9 +49,10 @@ def build(verbose: bool = False) -> str:
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
 
-    def one(src: str) -> str:
-        obj = os.path.join(objdir, src.rsplit(".", 1)[0] + ".o")
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    def one(item) -> str:
+        src, name, extra = item
+        obj = os.path.join(objdir, name + ".o")
+        cmd = [cc, *compile_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

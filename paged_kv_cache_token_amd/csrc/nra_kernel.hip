@@ -398,7 +398,7 @@ struct Cursor {
     }
 };
 
-template <int D, int QMODE, bool KVFP8, bool PART>
+template <int D, int QMODE, bool KVFP8, bool PART, bool STREAM>
 __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) {
     constexpr int G = D / 16;        // lanes per head row
     constexpr int RPW = 64 / G;      // head rows per wave
@@ -467,8 +467,13 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
             const int rr = ok ? r : 0;
             const int tt = ld.left > 0 ? ld.t : t_first;
             const uint16_t* src = a.qkv + (int64_t)tt * a.qkv_stride + rr * D;
-            buf[u][0] = ld16(src + lm.o0);
-            buf[u][1] = ld16(src + lm.o1);
+            if constexpr (STREAM) {
+                buf[u][0] = ld16_stream(src + lm.o0);
+                buf[u][1] = ld16_stream(src + lm.o1);
+            } else {
+                buf[u][0] = ld16(src + lm.o0);
+                buf[u][1] = ld16(src + lm.o1);
+            }
             ld.advance(CPT);
         }
     };
@@ -705,7 +710,7 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
 }
 
 // workgroups per CU the kernel can keep resident (queried once per device)
-template <int D, int QMODE, bool KVFP8, bool PART>
+template <int D, int QMODE, bool KVFP8, bool PART, bool STREAM>
 int resident_blocks(size_t lds) {
     static int cached_dev = -1, cached = 0, cached_cus = 0;
     static size_t cached_lds = (size_t)-1;
@@ -713,7 +718,7 @@ int resident_blocks(size_t lds) {
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (dev != cached_dev || lds != cached_lds) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nra_kernel<D, QMODE, KVFP8, PART>, kBlockThreads,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nra_kernel<D, QMODE, KVFP8, PART, STREAM>, kBlockThreads,
                                                          lds) != hipSuccess)
             per_cu = 1;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
@@ -726,13 +731,13 @@ int resident_blocks(size_t lds) {
     return cached;
 }
 
-template <int D, int QMODE, bool KVFP8, bool PART>
+template <int D, int QMODE, bool KVFP8, bool PART, bool STREAM>
 hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     size_t lds = a.paged ? (size_t)(3 * a.B + 2) * sizeof(int) : 0;
     if (a.stage_q_scale) lds = (size_t)((3 * a.B + 2 + 3) & ~3) * sizeof(int) + (size_t)kMaxTokensPerTile * a.Hq * sizeof(float);
     // enough workgroups to fill every CU, none with less than 8 head-row
     // chunks of work, and at least one per 4 requests for the tail clears
-    const int64_t cap = resident_blocks<D, QMODE, KVFP8, PART>(lds);
+    const int64_t cap = resident_blocks<D, QMODE, KVFP8, PART, STREAM>(lds);
     int64_t want = (a.total_items + 7) / 8;
     if (want < (a.B + 3) / 4) want = (a.B + 3) / 4;
     if (want < 1) want = 1;
@@ -744,26 +749,35 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     // HBM accesses of the moment close together (about 6 % faster on a
     // 15k-token prefill).  Short calls keep one contiguous range each.
     la.interleave = (a.T >= 8 * (int64_t)la.grid) ? 4 * a.chunks_per_token : 0;
-    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, PART>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
+    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, PART, STREAM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_norm_rope_append(const NraDevArgs& a, int head_dim, int q_mode, int kv_fp8,
-                                   hipStream_t stream) {
-#define QKPREP_NRA_CASE(DD, QM, KF) \
-    if (head_dim == DD && q_mode == QM && (kv_fp8 != 0) == KF)                                         \
-        return a.rot == DD ? launch_t<DD, QM, KF, false>(a, stream) : launch_t<DD, QM, KF, true>(a, stream);
-    QKPREP_NRA_CASE(64, 0, false) QKPREP_NRA_CASE(64, 0, true)
-    QKPREP_NRA_CASE(64, 1, false) QKPREP_NRA_CASE(64, 1, true)
-    QKPREP_NRA_CASE(64, 2, false) QKPREP_NRA_CASE(64, 2, true)
-    QKPREP_NRA_CASE(128, 0, false) QKPREP_NRA_CASE(128, 0, true)
-    QKPREP_NRA_CASE(128, 1, false) QKPREP_NRA_CASE(128, 1, true)
-    QKPREP_NRA_CASE(128, 2, false) QKPREP_NRA_CASE(128, 2, true)
-    QKPREP_NRA_CASE(256, 0, false) QKPREP_NRA_CASE(256, 0, true)
-    QKPREP_NRA_CASE(256, 1, false) QKPREP_NRA_CASE(256, 1, true)
-    QKPREP_NRA_CASE(256, 2, false) QKPREP_NRA_CASE(256, 2, true)
+#ifndef QKPREP_NRA_HEAD_DIM
+#error "nra_kernel.hip is compiled once per head dim with -DQKPREP_NRA_HEAD_DIM=64, 128 or 256"
+#endif
+#define QKPREP_CAT2(x, y) x##y
+#define QKPREP_CAT(x, y) QKPREP_CAT2(x, y)
+
+// Launch for head dim QKPREP_NRA_HEAD_DIM: picks the instance for the Q mode,
+// the cache dtype, whole-head or partial rotary, and streaming or cached
+// qkv loads.
+hipError_t QKPREP_CAT(launch_norm_rope_append_d, QKPREP_NRA_HEAD_DIM)(const NraDevArgs& a, int q_mode, int kv_fp8,
+                                                                       hipStream_t stream) {
+    constexpr int D = QKPREP_NRA_HEAD_DIM;
+#define QKPREP_NRA_CASE(QM, KF)                                                                          \
+    if (q_mode == QM && (kv_fp8 != 0) == KF) {                                                           \
+        if (a.rot == D)                                                                                  \
+            return a.stream_qkv ? launch_t<D, QM, KF, false, true>(a, stream)                             \
+                                : launch_t<D, QM, KF, false, false>(a, stream);                           \
+        return a.stream_qkv ? launch_t<D, QM, KF, true, true>(a, stream)                                  \
+                            : launch_t<D, QM, KF, true, false>(a, stream);                                \
+    }
+    QKPREP_NRA_CASE(0, false) QKPREP_NRA_CASE(0, true)
+    QKPREP_NRA_CASE(1, false) QKPREP_NRA_CASE(1, true)
+    QKPREP_NRA_CASE(2, false) QKPREP_NRA_CASE(2, true)
 #undef QKPREP_NRA_CASE
     return hipErrorInvalidValue;
 }

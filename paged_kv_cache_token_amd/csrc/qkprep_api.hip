@@ -164,6 +164,8 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     a.q_scale_inv = p->q_scale_inv;
     a.upper_max = p->upper_max;
     a.k_out = static_cast<uint16_t*>(p->k_out);
+    // qkv rows are read once unless Q or K is written back into them
+    a.stream_qkv = (p->q_out != p->qkv && p->k_out == nullptr) ? 1 : 0;
     a.k_out_stride = p->k_out_row_stride;
     a.flags = p->flags;
     const int rows_per_wave = 64 / (D / 16);

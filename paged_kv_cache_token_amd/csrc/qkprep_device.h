@@ -30,6 +30,14 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
+// Streaming load (non-temporal hint): for data read exactly once, so that it
+// does not displace what the caches hold for the writes in flight.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void st16(void* p, uint4 v) {
     *reinterpret_cast<uint4*>(p) = v;
 }

@@ -72,6 +72,7 @@ struct NraDevArgs {
     int32_t kv_group;
     float* k_scale_out;
     float* v_scale_out;
+    int32_t stream_qkv;                 // 1: qkv is read once (no Q/K written back): streaming loads
     int32_t interleave;                 // items per round-robin span, 0 = one range per workgroup
     int32_t grid;                       // workgroups launched (set by the launcher)
 };
@@ -109,8 +110,20 @@ struct MlaDevArgs {
 };
 
 // returns hipSuccess or the launch error
-hipError_t launch_norm_rope_append(const NraDevArgs& a, int head_dim, int q_mode, int kv_fp8,
-                                   hipStream_t stream);
+// one object of nra_kernel.hip per head dim
+hipError_t launch_norm_rope_append_d64(const NraDevArgs& a, int q_mode, int kv_fp8, hipStream_t stream);
+hipError_t launch_norm_rope_append_d128(const NraDevArgs& a, int q_mode, int kv_fp8, hipStream_t stream);
+hipError_t launch_norm_rope_append_d256(const NraDevArgs& a, int q_mode, int kv_fp8, hipStream_t stream);
+
+inline hipError_t launch_norm_rope_append(const NraDevArgs& a, int head_dim, int q_mode, int kv_fp8,
+                                          hipStream_t stream) {
+    switch (head_dim) {
+        case 64: return launch_norm_rope_append_d64(a, q_mode, kv_fp8, stream);
+        case 128: return launch_norm_rope_append_d128(a, q_mode, kv_fp8, stream);
+        case 256: return launch_norm_rope_append_d256(a, q_mode, kv_fp8, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 hipError_t launch_mla_concat_rope(const MlaDevArgs& a, int kv_fp8, hipStream_t stream);
 // FP8 Q modes: one workgroup per token at a time
 hipError_t launch_mla_q8(const MlaDevArgs& a, int kv_fp8, hipStream_t stream);
