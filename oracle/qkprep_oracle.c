@@ -304,10 +304,10 @@ static int nra_invalid(const oracle_nra_args *a)
         if (sl < qlen) return 1;
         if (sl > (int64_t)a->maxp * a->page_size) return 1;
         if (a->q_mode == 1 && a->q_scale_padded && qlen > a->max_seqlen) return 1;
-        /* pages this call writes: the appended rows, and the last page if
-         * its tail is cleared */
+        /* pages this call addresses: the appended rows, and the last page
+         * if its tail is cleared (never when K/V are redirected) */
         int64_t first_row = sl - qlen;
-        if (a->zero_tail && qlen == 0 && sl > 0) first_row = sl - 1;
+        if (a->zero_tail && !a->out_k && qlen == 0 && sl > 0) first_row = sl - 1;
         for (int64_t L = first_row; L < sl; ++L) {
             int32_t p = a->page_table[(int64_t)b * a->maxp + L / a->page_size];
             if (p < 0 || p >= a->num_pages) return 1;

@@ -162,7 +162,7 @@ class NraInputs:
             ql = int(self.q_indptr[b + 1] - self.q_indptr[b])
             sl = int(self.seq_lens[b])
             lo = sl - ql
-            if self.zero_tail and ql == 0 and sl > 0:
+            if self.zero_tail and not self.kv_redirect and ql == 0 and sl > 0:
                 lo = sl - 1
             if sl > lo:
                 pages.append(self.page_table[b, lo // self.page_size:(sl - 1) // self.page_size + 1])
