@@ -46,6 +46,12 @@ namespace qkprep {
 
 namespace {
 
+// Zeros that stand in for an input the call does not have (no tokens, no
+// norm weights, slot addressing...): every prologue load then goes out
+// unconditionally, with no lane mask or branch around it, which keeps the
+// compiler's in-order load counters exact.  Never written.
+__device__ __align__(16) const uint16_t g_zero_row[256] = {};
+
 // first index i in [0, n) with a[i] > key (a non-decreasing), n if none
 __device__ __forceinline__ int lds_upper_bound(const int* a, int n, int key) {
     int lo = 0, hi = n;
@@ -78,17 +84,22 @@ __device__ __forceinline__ ReqPages request_pages(const NraDevArgs& a, const int
     int lo_row = sl - ql;
     if (a.zero_tail && ql == 0 && sl > 0) lo_row = sl - 1;
     if (sl > lo_row) {
-        r.first = lo_row / a.page_size;
-        r.count = (sl - 1) / a.page_size - r.first + 1;
+        r.first = fdiv31(lo_row, a.ps_div);
+        r.count = fdiv31(sl - 1, a.ps_div) - r.first + 1;
     }
     return r;
 }
 
 // Validation, step 1 (LDS only): per-request checks and the block-wide
-// exclusive prefix s_pre[0..B] of the number of pages each request writes.
-// Needs s_indptr / s_seqlen staged.  Returns this thread's partial verdict.
+// exclusive prefix s_pre[0..B] of the number of pages each request writes,
+// with the request and page-table column of each of the first kPageSlots
+// pages (s_pgreq / s_pgcol).  Needs s_indptr / s_seqlen staged.  Returns
+// this thread's partial verdict.
+constexpr int kPageSlots = kBlockThreads;   // pages located by table lookup (one per thread)
+constexpr int kSearchRequests = 64;         // up to this many requests, pages are found by binary search
+
 __device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen, int* s_pre,
-                                 int* s_wave) {
+                                 int* s_wave, int* s_pgreq, int* s_pgcol) {
     const int tid = threadIdx.x;
     const int B = a.B;
     int bad = 0;
@@ -110,7 +121,15 @@ __device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const
     int run = base + incl - sum;
     for (int b = lo; b < hi; ++b) {
         s_pre[b] = run;
-        run += request_pages(a, s_indptr, s_seqlen, b).count;
+        const ReqPages rp = request_pages(a, s_indptr, s_seqlen, b);
+        // the first kPageSlots pages of the call: their request and column
+        // (many requests: each writes its few slots; few requests find their
+        // pages by binary search instead, see page_slot_ptr)
+        for (int k = run; a.B > kSearchRequests && k < min(run + rp.count, kPageSlots); ++k) {
+            s_pgreq[k] = b;
+            s_pgcol[k] = rp.first + (k - run);
+        }
+        run += rp.count;
     }
     if (tid == kBlockThreads - 1) s_pre[B] = base + incl;
     __syncthreads();
@@ -119,11 +138,16 @@ __device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const
 
 // Validation, step 2: every page id the call writes must lie in the pool.
 // Thread k checks pages k, k + 256, ...; page_id_at() issues one load.
-__device__ __forceinline__ int page_id_at(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen,
-                                          const int* s_pre, int k) {
+__device__ __forceinline__ const int* page_id_ptr(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen,
+                                                  const int* s_pre, int k) {
     const int b = lds_upper_bound(s_pre, a.B + 1, k) - 1;
     const ReqPages rp = request_pages(a, s_indptr, s_seqlen, b);
-    return a.page_table[(int64_t)b * a.maxp + rp.first + (k - s_pre[b])];
+    return a.page_table + (int64_t)b * a.maxp + rp.first + (k - s_pre[b]);
+}
+
+__device__ __forceinline__ int page_id_at(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen,
+                                          const int* s_pre, int k) {
+    return gld(page_id_ptr(a, s_indptr, s_seqlen, s_pre, k));
 }
 
 __device__ __forceinline__ int page_out_of_pool(const NraDevArgs& a, int p) {
@@ -399,7 +423,7 @@ struct Cursor {
 };
 
 template <int D, int QMODE, bool KVFP8, bool PART, bool STREAM>
-__global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) {
+__global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4))) void nra_kernel(const NraDevArgs a) {
     constexpr int G = D / 16;        // lanes per head row
     constexpr int RPW = 64 / G;      // head rows per wave
     constexpr int U = kBatch;
@@ -417,6 +441,9 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     __shared__ int64_t s_qsoff[kMaxTokensPerTile];
     __shared__ int64_t s_srow[kMaxTokensPerTile];    // cache row (page * page_size + row) or token, for K/V scales
     __shared__ int s_tail[kTailPrefetch];
+    __shared__ int s_pgreq[kPageSlots];              // request of page slot k
+    __shared__ int s_pgcol[kPageSlots];              // its page-table column
+    __shared__ int s_treq[kMaxTokensPerTile];        // request of each tile token
     __shared__ int s_flag[4];
 
     preload_kernargs(a);
@@ -466,7 +493,7 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
             const bool ok = ld.left > 0 && r < a.R;
             const int rr = ok ? r : 0;
             const int tt = ld.left > 0 ? ld.t : t_first;
-            const uint16_t* src = a.qkv + (int64_t)tt * a.qkv_stride + rr * D;
+            const uint16_t* src = (a.T > 0 ? a.qkv : g_zero_row) + (int64_t)tt * a.qkv_stride + rr * D;
             if constexpr (STREAM) {
                 buf[u][0] = ld16_stream(src + lm.o0);
                 buf[u][1] = ld16_stream(src + lm.o1);
@@ -490,26 +517,49 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
         ld.left = w_hi - w_lo;
         pr = ld;
     };
-    // per-token metadata that needs no request lookup (position, slot)
-    auto stage_positions = [&]() {
+    // request of every tile token, written by the threads that own the
+    // requests (each request covers one run of tokens); made visible by the
+    // next barrier.  Malformed metadata can leave entries unset: readers
+    // clamp, and the verdict rejects the call.
+    auto scatter_tokens = [&]() {
+        const int per = (a.B + kBlockThreads - 1) / kBlockThreads;
+        const int lo = min(a.B, tid * per), hi = min(a.B, lo + per);
+        for (int b = lo; b < hi; ++b) {
+            const int t0 = max(s_indptr[b], t_first), t1 = min(s_indptr[b + 1], t_first + ntok);
+            for (int t = t0; t < t1; ++t) s_treq[t - t_first] = b;
+        }
+    };
+    // per-token metadata that needs no request lookup (position, slot):
+    // fetched into registers, then written to LDS
+    struct TokMeta {
+        int64_t pos, slot;
+    };
+    // (every thread loads, at a clamped token, so that the loads carry no
+    // lane mask; only threads < ntok keep the result)
+    auto fetch_positions = [&]() {
+        const int t = t_first + max(min(tid, ntok - 1), 0);
+        // without rotated dims positions are not read and never suppress
+        const bool use_pos = a.rot > 0 && a.T > 0;
+        const bool use_slot = !a.paged && !a.redirect && a.T > 0;
+        const int64_t* pp = use_pos ? a.positions + t : reinterpret_cast<const int64_t*>(g_zero_row);
+        const int64_t* sp = use_slot ? a.slot_mapping + t : reinterpret_cast<const int64_t*>(g_zero_row);
+        const int64_t pv = gld(pp), sv = gld(sp);
+        return TokMeta{use_pos ? pv : 0, use_slot ? sv : -1};
+    };
+    auto store_positions = [&](const TokMeta& m) {
         if (tid < ntok) {
             const int t = t_first + tid;
-            // without rotated dims positions are not read and never suppress
-            const int64_t p64 = a.rot > 0 ? a.positions[t] : 0;
-            s_pos[tid] = (a.rot == 0 || (p64 >= 0 && p64 < a.cs_rows)) ? (int)p64 : -1;
+            s_pos[tid] = (a.rot == 0 || (m.pos >= 0 && m.pos < a.cs_rows)) ? (int)m.pos : -1;
             if (!a.paged) {
                 int64_t koff = -1, voff = -1, srow = -1;
                 if (a.redirect) {
                     koff = voff = (int64_t)t * a.kv_out_stride;
                     srow = t;
-                } else {
-                    const int64_t slot = a.slot_mapping[t];
-                    if (slot >= 0 && slot < (int64_t)a.num_pages * a.page_size) {
-                        const int64_t page = slot / a.page_size, row = slot % a.page_size;
-                        koff = page * a.k_page_stride + row * row_elems;
-                        voff = page * a.v_page_stride + row * row_elems;
-                        srow = slot;
-                    }
+                } else if (m.slot >= 0 && m.slot < (int64_t)a.num_pages * a.page_size) {
+                    const int64_t page = m.slot / a.page_size, row = m.slot % a.page_size;
+                    koff = page * a.k_page_stride + row * row_elems;
+                    voff = page * a.v_page_stride + row * row_elems;
+                    srow = m.slot;
                 }
                 s_koff[tid] = koff;
                 s_voff[tid] = voff;
@@ -518,58 +568,106 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
             }
         }
     };
-    // request lookup, page and cos/sin row of every tile token (needs s_pos)
-    auto stage_rows = [&]() {
-        if (a.paged && tid < ntok) {
-            // indices are clamped so that malformed metadata (rejected by the
-            // verdict computed alongside) still reads inside the page table
-            const int t = t_first + tid;
-            const int b = min(max(lds_upper_bound(s_indptr, a.B + 1, t) - 1, 0), a.B - 1);
+    auto stage_positions = [&]() { store_positions(fetch_positions()); };
+    // request lookup, page and cos/sin row of every tile token (needs s_pos):
+    // all loads issued first (unmasked, at clamped indices or from the zero
+    // row), then the LDS writes, so that the tile costs one round trip
+    constexpr int NCS = (kMaxTokensPerTile * D4 + kBlockThreads - 1) / kBlockThreads;   // float4 per thread
+    struct RowsFetch {
+        float4 cs[NCS];
+        int64_t page;
+        int b, j, L;
+    };
+    auto fetch_rows = [&]() {
+        RowsFetch f;
+#pragma unroll
+        for (int n = 0; n < NCS; ++n) {
+            // (the round count is the same for the whole workgroup)
+            if (n > 0 && n * kBlockThreads >= ntok * D4) break;
+            const int k = tid + n * kBlockThreads;
+            const int i = min(k / D4, kMaxTokensPerTile - 1);
+            const int c4 = k - (k / D4) * D4;
+            const int p = s_pos[i];
+            const bool ok = k < ntok * D4 && p >= 0 && 4 * c4 < a.rot;
+            f.cs[n] = ldf4(ok ? a.cos_sin + (int64_t)p * a.rot + 4 * c4 : reinterpret_cast<const float*>(g_zero_row));
+        }
+        // Indices are clamped so that malformed metadata (rejected by the
+        // verdict computed alongside) still reads inside the page table; only
+        // the load address is selected, so that no branch surrounds the load.
+        const int ti = max(min(tid, ntok - 1), 0);
+        const int t = t_first + ti;
+        f.b = f.j = f.L = 0;
+        if (a.paged) {
+            const int b = max(min(s_treq[ti], a.B - 1), 0);
             const int beg = s_indptr[b];
             const int ql = s_indptr[b + 1] - beg;
-            const int j = t - beg;
-            const int L = s_seqlen[b] - ql + j;
+            f.b = b;
+            f.j = t - beg;
+            f.L = s_seqlen[b] - ql + f.j;
+        }
+        const int pidx = min(max(fdiv31(max(f.L, 0), a.ps_div), 0), a.maxp - 1);
+        const bool use = a.paged && !a.redirect;
+        f.page = gld(use ? a.page_table + (int64_t)f.b * a.maxp + pidx : reinterpret_cast<const int*>(g_zero_row));
+        return f;
+    };
+    auto store_rows = [&](const RowsFetch& f) {
+#pragma unroll
+        for (int n = 0; n < NCS; ++n) {
+            const int k = tid + n * kBlockThreads;
+            const int i = k / D4;
+            const int c4 = k - i * D4;
+            if (k < ntok * D4 && s_pos[i] >= 0 && 4 * c4 < a.rot)
+                *reinterpret_cast<float4*>(s_cs + i * D + 4 * c4) = f.cs[n];
+        }
+        if (a.paged && tid < ntok) {
+            const int t = t_first + tid;
             if (a.redirect) {
                 s_koff[tid] = s_voff[tid] = (int64_t)t * a.kv_out_stride;
                 s_srow[tid] = t;
             } else {
-                const int pidx = min(max(L / a.page_size, 0), a.maxp - 1);
-                const int64_t page = a.page_table[(int64_t)b * a.maxp + pidx];
-                const int64_t row = L % a.page_size;
-                s_koff[tid] = page * a.k_page_stride + row * row_elems;
-                s_voff[tid] = page * a.v_page_stride + row * row_elems;
-                s_srow[tid] = page * a.page_size + row;
+                const int64_t row = f.L - fdiv31(max(f.L, 0), a.ps_div) * a.page_size;
+                s_koff[tid] = f.page * a.k_page_stride + row * row_elems;
+                s_voff[tid] = f.page * a.v_page_stride + row * row_elems;
+                s_srow[tid] = f.page * a.page_size + row;
             }
-            s_qsoff[tid] = a.q_scale_padded ? (int64_t)b * a.Hq * a.q_scale_P + j : (int64_t)t * a.Hq;
-        }
-        // table rows hold R floats (staged at a stride of D)
-        for (int k = tid; k < ntok * D4; k += kBlockThreads) {
-            const int i = k / D4;
-            const int c4 = k - i * D4;
-            const int p = s_pos[i];
-            if (p >= 0 && 4 * c4 < a.rot)
-                *reinterpret_cast<float4*>(s_cs + i * D + 4 * c4) = ldf4(a.cos_sin + (int64_t)p * a.rot + 4 * c4);
+            s_qsoff[tid] = a.q_scale_padded ? (int64_t)f.b * a.Hq * a.q_scale_P + f.j : (int64_t)t * a.Hq;
         }
     };
+    auto stage_rows = [&]() { store_rows(fetch_rows()); };
 
-    // page ids of the tails this workgroup clears (first kTailPrefetch requests)
+    // Requests of this workgroup (flags, and tail clears when there are more
+    // requests than workgroups).  With at least as many workgroups as
+    // requests, the tail of request blockIdx % B is instead split across all
+    // workgroups with that index: one workgroup clearing a whole 64-row
+    // page tail would start its token items late and end the kernel late.
     const int r_lo = (int)((int64_t)a.B * blockIdx.x / a.grid);
     const int r_hi = (int)((int64_t)a.B * (blockIdx.x + 1) / a.grid);
-    auto stage_tails = [&]() {
-        const int b = r_lo + tid;
-        if (tid < kTailPrefetch && b < r_hi) {
-            const int sl = s_seqlen[b];
-            const int pidx = min(max((sl - 1) / a.page_size, 0), a.maxp - 1);
-            s_tail[tid] = (a.zero_tail && sl > 0) ? a.page_table[(int64_t)b * a.maxp + pidx] : -1;
-        }
+    const bool tail_spread = a.paged && a.B <= a.grid;
+    const int t_req = tail_spread ? (int)(blockIdx.x % a.B) : 0;
+    const int t_slice = tail_spread ? (int)(blockIdx.x / a.B) : 0;
+    const int t_nslices = tail_spread ? (a.grid - 1 - t_req) / a.B + 1 : 1;
+    // page ids of the tails this workgroup clears (first kTailPrefetch requests)
+    auto fetch_tail = [&]() {
+        const int b = tail_spread ? t_req : min(r_lo + tid, max(r_hi - 1, 0));
+        const int sl = a.paged ? s_seqlen[min(b, a.B - 1)] : 0;
+        const int pidx = min(fdiv31(max(sl - 1, 0), a.ps_div), a.maxp - 1);
+        const bool use = a.paged && a.zero_tail && sl > 0;
+        return gld(use ? a.page_table + (int64_t)b * a.maxp + pidx : reinterpret_cast<const int*>(g_zero_row));
+    };
+    auto store_tail = [&](int page) {
+        const int b = tail_spread ? t_req : r_lo + tid;
+        if (tid < kTailPrefetch && (tail_spread ? tid == 0 : b < r_hi))
+            s_tail[tid] = (a.zero_tail && s_seqlen[b] > 0) ? page : -1;
     };
 
-    // device scalars of the call, loaded with the first round of metadata
+    // Device scalars of the call: the loads are issued here, with the first
+    // round of metadata, and the values are first used after its barrier
+    // (a reciprocal taken right away would wait for them on the spot).
+    const float k_scale_v = (KVFP8 && a.kv_group == 0) ? *a.k_scale : 1.0f;
+    const float v_scale_v = (KVFP8 && a.kv_group == 0) ? *a.v_scale : 1.0f;
+    const float q_static_v = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
     RowConsts kc;
-    kc.inv_k = (KVFP8 && a.kv_group == 0) ? 1.0f / *a.k_scale : 1.0f;
-    kc.inv_v = (KVFP8 && a.kv_group == 0) ? 1.0f / *a.v_scale : 1.0f;
     kc.kv_ng = a.kv_group ? D / a.kv_group : 0;
-    kc.q_static = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
     kc.inv_um = (QMODE == 1) ? 1.0f / a.upper_max : 1.0f;
     kc.qs_hstride = a.q_scale_padded ? (int)a.q_scale_P : 1;
     // Padded scales of consecutive tokens are 4-byte neighbours in each head's
@@ -578,36 +676,79 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     kc.s_qs = (QMODE == 1 && a.stage_q_scale)
                   ? reinterpret_cast<float*>(s_dyn + ((3 * a.B + 2 + 3) & ~3)) : nullptr;
 
-    // ---- first tile: its qkv loads go out before the metadata chain ----
+    // ---- first tile: its qkv loads go out with the first metadata round ----
+    // The request metadata, the norm weights and the tile's positions are
+    // loaded into registers first and the first qkv batch right after them:
+    // load counters retire in order, so waiting for the metadata then does
+    // not wait for the (much larger) qkv batch.
     const bool have_items = next_range();
     sub_lo = blo;
-    if (have_items) {
-        start_tile();
-        load_batch(bufA);
-    }
-    if (a.norm != 0) {
+    if (have_items) start_tile();
+    constexpr int WPT = (2 * D + kBlockThreads - 1) / kBlockThreads;   // norm weights per thread
+    {
+        // unmasked loads at clamped indices or from the zero row (a paged
+        // launch has B >= 1); request metadata up to 512 requests here
+        const float* zf = reinterpret_cast<const float*>(g_zero_row);
+        const int* zi = reinterpret_cast<const int*>(g_zero_row);
+        float wr[WPT];
+#pragma unroll
+        for (int k = 0; k < WPT; ++k) {
+            const int i = min(tid + k * kBlockThreads, 2 * D - 1);
+            wr[k] = gld(a.norm != 0 ? (i < D ? a.q_w + i : a.k_w + (i - D)) : zf);
+        }
+        int ip[2], sl[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int i = tid + k * kBlockThreads;
+            ip[k] = gld(a.paged ? a.q_indptr + min(i, a.B) : zi);
+            sl[k] = gld(a.paged ? a.seq_lens + min(i, a.B - 1) : zi);
+        }
+        const TokMeta m = fetch_positions();
+        load_batch(bufA);   // rows of token 0 (or zeros) when this workgroup has no items
         const float add = (a.norm == 2) ? 1.0f : 0.0f;
-        for (int i = tid; i < 2 * D; i += kBlockThreads) s_w[i] = (i < D ? a.q_w[i] : a.k_w[i - D]) + add;
+#pragma unroll
+        for (int k = 0; k < WPT; ++k) {
+            const int i = tid + k * kBlockThreads;
+            if (a.norm != 0 && i < 2 * D) s_w[i] = wr[k] + add;
+        }
+        if (a.paged) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int i = tid + k * kBlockThreads;
+                if (i <= a.B) s_indptr[i] = ip[k];
+                if (i < a.B) s_seqlen[i] = sl[k];
+            }
+            for (int i = tid + 2 * kBlockThreads; i <= a.B; i += kBlockThreads) s_indptr[i] = a.q_indptr[i];
+            for (int i = tid + 2 * kBlockThreads; i < a.B; i += kBlockThreads) s_seqlen[i] = a.seq_lens[i];
+        }
+        if (have_items) store_positions(m);
     }
-    if (a.paged) {
-        for (int i = tid; i <= a.B; i += kBlockThreads) s_indptr[i] = a.q_indptr[i];
-        for (int i = tid; i < a.B; i += kBlockThreads) s_seqlen[i] = a.seq_lens[i];
-    }
-    if (have_items) stage_positions();
     __syncthreads();
+    kc.inv_k = 1.0f / k_scale_v;
+    kc.inv_v = 1.0f / v_scale_v;
+    kc.q_static = q_static_v;
     int bad = 0;
-    if (a.paged) bad = validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave);
+    if (a.paged) {
+        scatter_tokens();   // made visible by the barriers inside the validation
+        bad = validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave, s_pgreq, s_pgcol);
+    }
     {
         // The page-id checks, the tile's row lookups and cos/sin loads and the
         // tail-page prefetch are independent and all issue at once.  Page
         // reads stay inside the page table even for malformed metadata (the
         // page counts of an inconsistent request are zero and the row lookups
         // are clamped); nothing is written unless the whole call is valid.
-        int p_first = 0;
         const int total_pages = a.paged ? s_pre[a.B] : 0;
-        if (tid < total_pages) p_first = page_id_at(a, s_indptr, s_seqlen, s_pre, tid);
-        if (have_items) stage_rows();
-        if (a.paged) stage_tails();
+        const int ks = min(tid, max(min(total_pages, kPageSlots) - 1, 0));
+        const int* pp = reinterpret_cast<const int*>(g_zero_row);
+        if (total_pages > 0)
+            pp = a.B > kSearchRequests ? a.page_table + (int64_t)s_pgreq[ks] * a.maxp + s_pgcol[ks]
+                                       : page_id_ptr(a, s_indptr, s_seqlen, s_pre, ks);
+        const int p_first = gld(pp);
+        const RowsFetch rf = fetch_rows();
+        const int tail_page = fetch_tail();
+        if (have_items) store_rows(rf);
+        if (a.paged) store_tail(tail_page);
         if (tid < total_pages) bad |= page_out_of_pool(a, p_first);
         for (int k = tid + kBlockThreads; k < total_pages; k += kBlockThreads)
             bad |= page_out_of_pool(a, page_id_at(a, s_indptr, s_seqlen, s_pre, k));
@@ -632,22 +773,18 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
     // ------------------ requests: flags and tail clear ------------------
     // (issued before the token items so the zero stores drain while the
     // rows are processed)
-    for (int b = r_lo; a.paged && b < r_hi; ++b) {
-        for (int h = tid; h < a.Hkv; h += kBlockThreads) a.flags[(int64_t)b * a.Hkv + h] = bad ? -1 : 0;
-        if (bad || !a.zero_tail) continue;
-        const int sl = s_seqlen[b];
-        if (sl <= 0) continue;
-        const int last = (sl - 1) % a.page_size;
-        const int64_t page = (b - r_lo < kTailPrefetch)
-                                 ? (int64_t)s_tail[b - r_lo]
-                                 : (int64_t)a.page_table[(int64_t)b * a.maxp + (sl - 1) / a.page_size];
+    // slice `slice` of `nslices` of the tail rows of request b (seq_len sl > 0)
+    auto clear_tail = [&](int sl, int64_t page, int slice, int nslices) {
+        const int pcol = fdiv31(sl - 1, a.ps_div);
+        const int last = (sl - 1) - pcol * a.page_size;
         const int64_t nvec = (int64_t)(a.page_size - 1 - last) * row_elems * (int64_t)sizeof(kv_t) / 16;
         char* kb = reinterpret_cast<char*>(reinterpret_cast<kv_t*>(a.k_cache) + page * a.k_page_stride +
                                            (last + 1) * row_elems);
         char* vb = reinterpret_cast<char*>(reinterpret_cast<kv_t*>(a.v_cache) + page * a.v_page_stride +
                                            (last + 1) * row_elems);
         const uint4 z = make_uint4(0, 0, 0, 0);
-        for (int64_t i = tid; i < nvec; i += kBlockThreads) {
+        const int64_t v1 = nvec * (slice + 1) / nslices;
+        for (int64_t i = nvec * slice / nslices + tid; i < v1; i += kBlockThreads) {
             st16(kb + 16 * i, z);
             st16(vb + 16 * i, z);
         }
@@ -656,12 +793,29 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
             const int64_t ns = (int64_t)a.Hkv * kc.kv_ng;
             const int64_t first = (page * a.page_size + last + 1) * ns;
             const int64_t cnt = (int64_t)(a.page_size - 1 - last) * ns;
-            for (int64_t i = tid; i < cnt; i += kBlockThreads) {
+            const int64_t c1 = cnt * (slice + 1) / nslices;
+            for (int64_t i = cnt * slice / nslices + tid; i < c1; i += kBlockThreads) {
                 a.k_scale_out[first + i] = 0.0f;
                 a.v_scale_out[first + i] = 0.0f;
             }
         }
+    };
+    for (int b = r_lo; a.paged && b < r_hi; ++b) {
+        for (int h = tid; h < a.Hkv; h += kBlockThreads) a.flags[(int64_t)b * a.Hkv + h] = bad ? -1 : 0;
+        if (bad || !a.zero_tail || tail_spread) continue;
+        const int sl = s_seqlen[b];
+        if (sl <= 0) continue;
+        // (an LDS read for the prefetched pages; a select between the two
+        // would become a flat load whose wait drains every store in flight)
+        int64_t page;
+        if (b - r_lo < kTailPrefetch)
+            page = s_tail[b - r_lo];
+        else
+            page = gld(a.page_table + (int64_t)b * a.maxp + fdiv31(sl - 1, a.ps_div));
+        clear_tail(sl, page, 0, 1);
     }
+    if (tail_spread && !bad && a.zero_tail && s_seqlen[t_req] > 0)
+        clear_tail(s_seqlen[t_req], s_tail[0], t_slice, t_nslices);
 
     // ---------------------------- token items ----------------------------
     if (have_items && !bad) {
@@ -696,10 +850,14 @@ __global__ __launch_bounds__(kBlockThreads) void nra_kernel(const NraDevArgs a) 
                 if (!next_range()) break;
                 sub_lo = blo;
             }
-            __syncthreads();   // every wave is done with this tile's LDS rows
             start_tile();
+            // positions first, then the qkv batch: the wait for the positions
+            // (load counters retire in order) then excludes the batch
+            const TokMeta m = fetch_positions();
             load_batch(bufA);
-            stage_positions();
+            __syncthreads();   // every wave is done with the previous tile's LDS rows
+            store_positions(m);
+            if (a.paged) scatter_tokens();
             __syncthreads();
             stage_rows();
             __syncthreads();

@@ -152,6 +152,7 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     a.kv_group = kv_group;
     a.k_scale_out = p->k_scale_out; a.v_scale_out = p->v_scale_out;
     a.num_pages = p->num_pages; a.page_size = p->page_size;
+    a.ps_div = make_fastdiv31((uint32_t)p->page_size);
     a.k_page_stride = p->k_page_stride; a.v_page_stride = p->v_page_stride;
     a.k_scale = p->k_scale; a.v_scale = p->v_scale;
     a.zero_tail = paged && !redirect && p->zero_tail ? 1 : 0;

@@ -26,15 +26,28 @@ constexpr float kE4M3Max = 448.0f;
 // memory
 // ---------------------------------------------------------------------------
 
+// Loads through the global address space: a pointer chosen between two
+// buffers (or built from a generic pointer) would otherwise be loaded with a
+// flat instruction, whose wait also drains every outstanding load.
+// (scalar and ext-vector types; the C-style cast is an address-space cast)
+template <typename T>
+__device__ __forceinline__ T gld(const T* p) {
+    typedef const __attribute__((address_space(1))) T gT;
+    return *(gT*)p;
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint4 ld16(const void* p) {
-    return *reinterpret_cast<const uint4*>(p);
+    const u32x4_t v = gld(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Streaming load (non-temporal hint): for data read exactly once, so that it
 // does not displace what the caches hold for the writes in flight.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16_stream(const void* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    typedef const __attribute__((address_space(1))) u32x4_t gT;
+    const u32x4_t v = __builtin_nontemporal_load((gT*)p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -46,8 +59,11 @@ __device__ __forceinline__ void st8(void* p, uint2 v) {
     *reinterpret_cast<uint2*>(p) = v;
 }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float4 ldf4(const float* p) {
-    return *reinterpret_cast<const float4*>(p);
+    const f32x4_t v = gld(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
 }
 
 // Touch every dword of a kernel-argument struct at kernel entry.  The
@@ -60,6 +76,15 @@ __device__ __forceinline__ void preload_kernargs(const T& args) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(&args);
 #pragma unroll
     for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(w[i]));
+}
+
+// n / d for 0 <= n < 2^31 with the host-computed multiplier of
+// make_fastdiv31 (the sum below stays under 2^32)
+struct FastDiv31;
+template <typename FD>
+__device__ __forceinline__ int fdiv31(int n, const FD& f) {
+    const uint32_t t = __umulhi((uint32_t)n, f.m);
+    return (int)((t + (uint32_t)n) >> f.l);
 }
 
 // ---------------------------------------------------------------------------

@@ -20,6 +20,26 @@ constexpr int kBatch = 2;
 // tail pages of the first requests a workgroup clears, prefetched with the metadata
 constexpr int kTailPrefetch = 16;
 
+// Division of a non-negative 31-bit integer by a runtime divisor d >= 1
+// without a division instruction (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", round-up variant):
+// l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l.
+struct FastDiv31 {
+    uint32_t m;
+    uint32_t l;
+    uint32_t d;
+};
+
+inline FastDiv31 make_fastdiv31(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    FastDiv31 f;
+    f.m = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+    f.l = l;
+    f.d = d;
+    return f;
+}
+
 struct NraDevArgs {
     // shapes
     int32_t T, Hq, Hkv, R;             // R = Hq + 2 Hkv head rows per token
@@ -44,6 +64,7 @@ struct NraDevArgs {
     void* k_cache;
     void* v_cache;
     int32_t num_pages, page_size;
+    FastDiv31 ps_div;                   // division by page_size
     int64_t k_page_stride, v_page_stride;
     const float* k_scale;
     const float* v_scale;
