@@ -102,7 +102,10 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     const int CPT = a.chunks_per_token;
     const int n_qchunks = CPT - 1;
     const int TPB = a.tokens_per_tile;
-    const float inv_scale = KVFP8 ? 1.0f / *a.kv_scale : 1.0f;
+    // the scale's load is issued here and its reciprocal taken after the
+    // first barrier (taken right away, it would wait for the load on the spot)
+    const float kv_scale_v = KVFP8 ? *a.kv_scale : 1.0f;
+    float inv_scale = 1.0f;
     kv_t* cache = reinterpret_cast<kv_t*>(a.kv_cache);
 
     const int blo = (int)((int64_t)a.total_items * blockIdx.x / a.grid);
@@ -144,24 +147,30 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
         ld.left = w_hi - w_lo;
         pr = ld;
     };
+    // Tile metadata, in one chain of two rounds with the tile's first q batch
+    // issued alongside: every thread loads the position of the cos/sin row
+    // piece it stages (thread k: token k / 16, float4 k % 16; ntok <= 16
+    // tokens x 16 float4 = 256) and thread i < ntok the token's slot, all
+    // unmasked at clamped indices; then the qkv batch; then the cos/sin
+    // loads, which need the positions.
+    static_assert(kMaxTokensPerTile * (kRope / 4) <= kBlockThreads, "one cos/sin float4 per thread");
     auto stage_tile = [&]() {
+        const int ic = min(tid / (kRope / 4), ntok - 1);
+        const int c4 = tid % (kRope / 4);
+        const int it = min(tid, ntok - 1);
+        const int64_t pc = gld(a.positions + t_first + ic);
+        const int64_t pt = gld(a.positions + t_first + it);
+        const int64_t slot = gld(a.slot_mapping + t_first + it);
+        load_batch(bufA);
+        const bool pc_ok = pc >= 0 && pc < a.cs_rows;
+        const float4 cs = ldf4(a.cos_sin + (pc_ok ? pc : 0) * kRope + 4 * c4);
         if (tid < ntok) {
-            const int t = t_first + tid;
-            const int64_t p64 = a.positions[t];
-            const int64_t slot = a.slot_mapping[t];
-            s_pos[tid] = (p64 >= 0 && p64 < a.cs_rows) ? (int)p64 : -1;
+            s_pos[tid] = (pt >= 0 && pt < a.cs_rows) ? (int)pt : -1;
             s_row[tid] = (slot >= 0 && slot < a.capacity)
                              ? (slot / a.block_size) * a.block_stride + (slot % a.block_size) * (int64_t)row_len
                              : -1;
         }
-        // cos/sin rows (positions read again: the LDS copy is not yet visible)
-        for (int k = tid; k < ntok * (kRope / 4); k += kBlockThreads) {
-            const int i = k / (kRope / 4);
-            const int c4 = k - i * (kRope / 4);
-            const int64_t p64 = a.positions[t_first + i];
-            if (p64 >= 0 && p64 < a.cs_rows)
-                *reinterpret_cast<float4*>(s_cs + i * kRope + 4 * c4) = ldf4(a.cos_sin + p64 * kRope + 4 * c4);
-        }
+        if (tid < ntok * (kRope / 4) && pc_ok) *reinterpret_cast<float4*>(s_cs + ic * kRope + 4 * c4) = cs;
     };
     auto run_batch = [&](uint4 (&buf)[U][2]) {
 #pragma unroll
@@ -237,9 +246,9 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     for (bool first = true; sub_lo < bhi; first = false) {
         if (!first) __syncthreads();   // every wave is done with the previous tile's LDS
         start_tile();
-        load_batch(bufA);
         stage_tile();
         __syncthreads();
+        inv_scale = KVFP8 ? 1.0f / kv_scale_v : 1.0f;
         while (pr.left > 0) {
             load_batch(bufB);
             run_batch(bufA);
@@ -313,7 +322,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
     const int rounds = (a.H + 63) >> 6;
     const float q_static = (QMODE == 2) ? *a.q_scale_inv : 1.0f;
     const float inv_um = (QMODE == 1) ? 1.0f / a.upper_max : 1.0f;
-    const float inv_kv = KVFP8 ? 1.0f / *a.kv_scale : 1.0f;
+    const float kv_scale_v = KVFP8 ? *a.kv_scale : 1.0f;   // reciprocal taken where first used
     kv_t* cache = reinterpret_cast<kv_t*>(a.kv_cache);
     int par = 0;   // s_amax slot: consecutive reductions alternate, so one barrier each suffices
 
@@ -420,7 +429,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                 if constexpr (KVFP8) {
                     float x[8];
                     unpack8(kvv, x);
-                    st8(dst + 8 * lane, pack8_fp8(x, inv_kv));
+                    st8(dst + 8 * lane, pack8_fp8(x, 1.0f / kv_scale_v));
                 } else {
                     st16(dst + 8 * lane, kvv);
                 }
@@ -429,7 +438,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                     if constexpr (KVFP8) {
                         float x[8];
                         unpack8(v, x);
-                        st8(dst + e, pack8_fp8(x, inv_kv));
+                        st8(dst + e, pack8_fp8(x, 1.0f / kv_scale_v));
                     } else {
                         st16(dst + e, v);
                     }
@@ -440,8 +449,8 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                     unpack8(pe_hi, x + 8);
                     rope16(x, c, s, a.rope);
                     if constexpr (KVFP8) {
-                        store_fp8_row(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf, pack8_fp8(x, inv_kv),
-                                      pack8_fp8(x + 8, inv_kv));
+                        store_fp8_row(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf,
+                                      pack8_fp8(x, 1.0f / kv_scale_v), pack8_fp8(x + 8, 1.0f / kv_scale_v));
                     } else {
                         st16(dst + K + 8 * gl, pack8_bf16(x));
                         st16(dst + K + kHalf + 8 * gl, pack8_bf16(x + 8));
