@@ -344,6 +344,43 @@ def test_many_requests_cross_page_ragged():
     run_and_compare(inp)
 
 
+def test_maximum_request_count():
+    """B = 4096 (the most the kernel stages): request metadata beyond the
+    first 512 entries, page slots beyond the first 256, more requests than
+    workgroups for the tail clears."""
+    rng = np.random.default_rng(4096)
+    B = 4096
+    q = rng.integers(0, 3, size=B)
+    prior = rng.integers(0, 50, size=B)
+    inp = W.nra_case(seed=4096, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=16)
+    run_and_compare(inp)
+
+
+def test_maximum_request_count_with_one_bad_request():
+    rng = np.random.default_rng(4097)
+    B = 4096
+    q = rng.integers(1, 3, size=B)
+    prior = rng.integers(0, 50, size=B)
+    inp = W.nra_case(seed=4097, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=16)
+    inp.seq_lens = inp.seq_lens.copy()
+    inp.seq_lens[4000] = 0                      # below its q_len: the whole call is invalid
+    stats = run_and_compare(inp)
+    assert stats == {} or "q" not in stats
+
+
+def test_requests_spread_tails_with_scattered_page_slots():
+    """100 requests (page slots found by scatter) and more workgroups than
+    requests (each page-64 tail split across workgroups)."""
+    rng = np.random.default_rng(100)
+    q = rng.integers(20, 60, size=100)
+    q[[3, 50]] = 0
+    prior = rng.integers(0, 300, size=100)
+    inp = W.nra_case(seed=100, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=64,
+                     kv_fp8=True, k_scale=0.05, v_scale=0.05, q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=True,
+                     max_seqlen=64)
+    run_and_compare(inp)
+
+
 # ----------------------------------------------------------------------------
 # MLA variants
 # ----------------------------------------------------------------------------
