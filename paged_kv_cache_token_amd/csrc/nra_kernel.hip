@@ -205,11 +205,13 @@ __device__ __forceinline__ void store_fp8_lane(uint8_t* row, int gl, const LaneM
     uint2 recv;
     recv.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.x, kDppQuadSwap1, 0xF, 0xF, false);
     recv.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.y, kDppQuadSwap1, 0xF, 0xF, false);
-    if (m.fp8_store == 1) {
-        const uint4 v = odd ? make_uint4(recv.x, recv.y, hi.x, hi.y) : make_uint4(lo.x, lo.y, recv.x, recv.y);
-        st16(row + (odd ? m.o1 - 8 : m.o0), v);
-    } else if (m.fp8_store == 0) {
-        st16(row + m.o0, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    if (m.fp8_store != 2) {
+        // paired rope lanes and pass-through lanes in one store instruction,
+        // so a row's 128-byte lines are written by a single instruction
+        const bool swap = m.fp8_store == 1;
+        const uint4 v = !swap ? make_uint4(lo.x, lo.y, hi.x, hi.y)
+                        : odd ? make_uint4(recv.x, recv.y, hi.x, hi.y) : make_uint4(lo.x, lo.y, recv.x, recv.y);
+        st16(row + ((swap && odd) ? m.o1 - 8 : m.o0), v);
     } else {
         st8(row + m.o0, lo);
         st8(row + m.o1, hi);
@@ -901,12 +903,17 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     if (want < 1) want = 1;
     NraDevArgs la = a;
     la.grid = (int)(want < cap ? want : cap);
-    // Long calls (8 or more tokens per workgroup) deal 4-token spans
+    // Long calls (8 or more tokens per workgroup) deal spans of tokens
     // round-robin: the resident workgroups then stream through one window of
     // qkv and the caches instead of the whole call at once, which keeps the
     // HBM accesses of the moment close together (about 6 % faster on a
-    // 15k-token prefill).  Short calls keep one contiguous range each.
-    la.interleave = (a.T >= 8 * (int64_t)la.grid) ? 4 * a.chunks_per_token : 0;
+    // 15k-token prefill).  A span is 4 tokens, or about 48 chunks when the
+    // tokens are short (few head rows per token), so that the per-tile
+    // metadata round is spread over enough rows.  Short calls keep one
+    // contiguous range each.
+    const int cpt = a.chunks_per_token;
+    const int span_tok = cpt >= 8 ? 4 : min(kMaxTokensPerTile, (48 + cpt - 1) / cpt);
+    la.interleave = (a.T >= 8 * (int64_t)la.grid) ? span_tok * cpt : 0;
     hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, PART, STREAM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();
 }
