@@ -295,8 +295,9 @@ hipError_t launch_t(const MlaDevArgs& a, hipStream_t stream) {
 //
 // A workgroup takes whole tokens (t = blockIdx.x, + grid, ...), so the
 // token's amax is one workgroup reduction (one barrier).  Four lanes own a
-// head: lane l loads the NV = nope_dim / 32 nope vectors [8 l NV, 8 (l+1) NV)
-// and the rope vectors [8l, 8l+8), [32 + 8l, 32 + 8l + 8); a wave covers 16
+// head: lane l loads the NV = nope_dim / 32 nope vectors l, l + 4, ... (8
+// elements each) and the rope vectors [8l, 8l+8), [32 + 8l, 32 + 8l + 8), so
+// every load instruction covers 64 contiguous bytes of a head; a wave covers 16
 // heads, a workgroup 64 per round, and two rounds (128 heads) are held in
 // registers.  The token's cos/sin values are read straight into registers
 // (every head uses the same 16 per lane).  One wave also writes the
@@ -350,7 +351,9 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                 hh[k] = h;
                 const uint16_t* qh = qt + (int64_t)(h < a.H ? h : 0) * a.q_head_stride;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) vn[k][j] = j < NV ? ld16(qh + 8 * (gl * NV + j)) : make_uint4(0, 0, 0, 0);
+                // nope vector j of lane gl: elements [8 (gl + 4 j), +8), so that
+                // each load instruction reads 64 contiguous bytes of a head
+                for (int j = 0; j < 4; ++j) vn[k][j] = j < NV ? ld16(qh + 8 * (gl + 4 * j)) : make_uint4(0, 0, 0, 0);
                 vr[k][0] = ld16(qh + N + 8 * gl);
                 vr[k][1] = ld16(qh + N + kHalf + 8 * gl);
             }
@@ -393,14 +396,15 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                 if (hh[k] >= a.H) continue;   // whole 4-lane group skips together
                 uint8_t* oh = ot + (int64_t)hh[k] * a.q_out_head_stride;
                 if ((NV & 1) == 0) {
+                    // codes of vectors j and j + 1 lie 32 bytes apart: neighbouring
+                    // lanes trade one 8-byte piece and each stores 16 bytes
 #pragma unroll
                     for (int j = 0; j < 4; j += 2) {
                         if (j < NV) {
                             float x[16];
                             unpack8(vn[k][j], x);
                             unpack8(vn[k][j + 1], x + 8);
-                            const uint2 lo = pack8_fp8(x, mul), hi = pack8_fp8(x + 8, mul);
-                            st16(oh + 8 * (gl * NV + j), make_uint4(lo.x, lo.y, hi.x, hi.y));
+                            store_fp8_row(oh + 32 * j, gl, 32, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
                         }
                     }
                 } else {
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                         if (j < NV) {
                             float x[8];
                             unpack8(vn[k][j], x);
-                            st8(oh + 8 * (gl * NV + j), pack8_fp8(x, mul));
+                            st8(oh + 8 * (gl + 4 * j), pack8_fp8(x, mul));
                         }
                     }
                 }
