@@ -220,22 +220,26 @@ __device__ __forceinline__ void store_fp8_lane(uint8_t* row, int gl, const LaneM
 
 // max over aligned groups of n lanes (n = 1, 2, 4, 8 or 16, the same for
 // the whole wave); every lane of a group receives the group's max
+// (non-negative values: the reduction runs on their bit patterns)
 __device__ __forceinline__ float subgroup_max(float v, int n) {
-    if (n >= 2) v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap1>(v));
-    if (n >= 4) v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap2>(v));
-    if (n >= 8) v = __builtin_fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
-    if (n >= 16) v = __builtin_fmaxf(v, dpp_f<kDppRowMirror>(v));
-    return v;
+    uint32_t u = __float_as_uint(v);
+    if (n >= 2) u = max(u, dpp_u<kDppQuadSwap1>(u));
+    if (n >= 4) u = max(u, dpp_u<kDppQuadSwap2>(u));
+    if (n >= 8) u = max(u, dpp_u<kDppRowHalfMirror>(u));
+    if (n >= 16) u = max(u, dpp_u<kDppRowMirror>(u));
+    return __uint_as_float(u);
 }
 
 // E4M3 codes of a K or V head row with dynamic scales: one per group of
-// a.kv_group dims, s = max(amax, 1e-6) / 448, stored at sc[group].  With
-// a.kv_group == D the whole row shares one scale; smaller groups lie inside
-// one half of the lane split (whole-head rotary layout: the lane holds dims
-// [8 gl, 8 gl + 8) and [D/2 + 8 gl, D/2 + 8 gl + 8)) and span g/8 lanes.
+// a.kv_group dims, s = max(amax, 1e-6) / 448, stored at sc[group].  The row
+// is f * x (f > 0: the RMSNorm factor not yet applied to x, or 1), so the
+// amax is f * max|x| and the payload multiplier f / s.  With a.kv_group == D
+// the whole row shares one scale; smaller groups lie inside one half of the
+// lane split (whole-head rotary layout: the lane holds dims [8 gl, 8 gl + 8)
+// and [D/2 + 8 gl, D/2 + 8 gl + 8)) and span g/8 lanes.
 template <int D>
-__device__ __forceinline__ void kv_fp8_dynamic(const NraDevArgs& a, int gl, const float* x, float* sc, uint2& lo,
-                                               uint2& hi) {
+__device__ __forceinline__ void kv_fp8_dynamic(const NraDevArgs& a, int gl, const float* x, float f, float* sc,
+                                               uint2& lo, uint2& hi) {
     constexpr int G = D / 16;
     constexpr float kInv448 = 1.0f / 448.0f;
     float m0 = 0.0f, m1 = 0.0f;
@@ -245,21 +249,21 @@ __device__ __forceinline__ void kv_fp8_dynamic(const NraDevArgs& a, int gl, cons
         m1 = __builtin_fmaxf(m1, __builtin_fabsf(x[8 + i]));
     }
     if (a.kv_group == D) {
-        const float s = __builtin_fmaxf(group_max<G>(__builtin_fmaxf(m0, m1)), 1e-6f) * kInv448;
-        const float mul = __builtin_amdgcn_rcpf(s);
+        const float s = max_nonneg(group_max<G>(max_nonneg(m0, m1)) * f, 1e-6f) * kInv448;
+        const float mul = f * __builtin_amdgcn_rcpf(s);
         if (gl == 0) sc[0] = s;
-        lo = pack8_fp8(x, mul);
-        hi = pack8_fp8(x + 8, mul);
+        lo = pack8_fp8_bounded(x, mul);
+        hi = pack8_fp8_bounded(x + 8, mul);
     } else {
         const int n = a.kv_group >> 3;
-        const float s0 = __builtin_fmaxf(subgroup_max(m0, n), 1e-6f) * kInv448;
-        const float s1 = __builtin_fmaxf(subgroup_max(m1, n), 1e-6f) * kInv448;
+        const float s0 = max_nonneg(subgroup_max(m0, n) * f, 1e-6f) * kInv448;
+        const float s1 = max_nonneg(subgroup_max(m1, n) * f, 1e-6f) * kInv448;
         if ((gl & (n - 1)) == 0) {
             sc[(8 * gl) / a.kv_group] = s0;
             sc[(D / 2 + 8 * gl) / a.kv_group] = s1;
         }
-        lo = pack8_fp8(x, __builtin_amdgcn_rcpf(s0));
-        hi = pack8_fp8(x + 8, __builtin_amdgcn_rcpf(s1));
+        lo = pack8_fp8_bounded(x, f * __builtin_amdgcn_rcpf(s0));
+        hi = pack8_fp8_bounded(x + 8, f * __builtin_amdgcn_rcpf(s1));
     }
 }
 
@@ -294,7 +298,7 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
             unpack8(v1, x + 8);
             uint2 lo, hi;
             if (k.kv_ng) {
-                kv_fp8_dynamic<D>(a, gl, x, a.v_scale_out + (s_srow[ti] * a.Hkv + vh) * k.kv_ng, lo, hi);
+                kv_fp8_dynamic<D>(a, gl, x, 1.0f, a.v_scale_out + (s_srow[ti] * a.Hkv + vh) * k.kv_ng, lo, hi);
             } else {
                 lo = pack8_fp8(x, k.inv_v);
                 hi = pack8_fp8(x + 8, k.inv_v);
@@ -310,12 +314,19 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
     float x[16];
     unpack8(v0, x);
     unpack8(v1, x + 8);
+    // RMSNorm factor not yet applied to x.  Rows that end as E4M3 (and
+    // write no bf16 copy) apply it with their payload multiplier, after
+    // RoPE (which is linear): one multiply per element fewer.  bf16 rows
+    // apply it here.
+    float f = 1.0f;
     if (a.norm != 0) {
         float ss = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) ss = fmaf(x[i], x[i], ss);
         ss = group_sum<G>(ss);
-        const float inv = rsqrtf(fmaf(ss, 1.0f / (float)D, a.eps));
+        // the argument is >= eps > 0; the floor keeps v_rsq off denormal
+        // inputs (an all-zero row with eps < 2^-126 stays zero)
+        const float inv = __builtin_amdgcn_rsqf(__builtin_fmaxf(fmaf(ss, 1.0f / (float)D, a.eps), 1.17549435e-38f));
         const float* w = s_w + (is_q ? 0 : D);
         const float4 w0 = *reinterpret_cast<const float4*>(w + lm.o0);
         const float4 w1 = *reinterpret_cast<const float4*>(w + lm.o0 + 4);
@@ -323,8 +334,15 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
         const float4 w3 = *reinterpret_cast<const float4*>(w + lm.o1 + 4);
         const float wv[16] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w,
                               w2.x, w2.y, w2.z, w2.w, w3.x, w3.y, w3.z, w3.w};
+        const bool late = is_q ? QMODE != 0 : (KVFP8 && a.k_out == nullptr);
+        if (late) {
+            f = inv;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = x[i] * inv * wv[i];
+            for (int i = 0; i < 16; ++i) x[i] = x[i] * wv[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = x[i] * inv * wv[i];
+        }
     }
     if (lm.rope) {
         const int hr = lm.hr;
@@ -369,21 +387,24 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
             st16(row + lm.o1, pack8_bf16(x + 8));
         } else {
             uint8_t* row = reinterpret_cast<uint8_t*>(a.q_out) + (int64_t)t * a.q_out_stride + h * D;
-            float mul = k.q_static;
             if constexpr (QMODE == 1) {
+                // the row is f * x: amax = f * max|x|, s = max(amax, 1e-6) /
+                // upper_max, payload = x * (f / s)
                 float amax = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
-                amax = group_max<G>(amax);
-                // s = max(amax, 1e-6) / upper_max; payload = x * (1 / s)
-                const float sc = __builtin_fmaxf(amax, 1e-6f) * k.inv_um;
-                mul = __builtin_amdgcn_rcpf(sc);
+                amax = group_max<G>(amax) * f;
+                const float sc = max_nonneg(amax, 1e-6f) * k.inv_um;
+                const float mul = f * __builtin_amdgcn_rcpf(sc);
                 if (gl == 0) {
                     if (k.s_qs) k.s_qs[ti * a.Hq + h] = sc;
                     else a.q_scale[s_qsoff[ti] + (int64_t)h * k.qs_hstride] = sc;
                 }
+                store_fp8_lane(row, gl, lm, pack8_fp8_bounded(x, mul), pack8_fp8_bounded(x + 8, mul));
+            } else {
+                const float mul = f * k.q_static;
+                store_fp8_lane(row, gl, lm, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
             }
-            store_fp8_lane(row, gl, lm, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
         }
     } else {
         const int kh = r - a.Hq;
@@ -393,10 +414,10 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
             if constexpr (KVFP8) {
                 uint2 lo, hi;
                 if (k.kv_ng) {
-                    kv_fp8_dynamic<D>(a, gl, x, a.k_scale_out + (s_srow[ti] * a.Hkv + kh) * k.kv_ng, lo, hi);
+                    kv_fp8_dynamic<D>(a, gl, x, f, a.k_scale_out + (s_srow[ti] * a.Hkv + kh) * k.kv_ng, lo, hi);
                 } else {
-                    lo = pack8_fp8(x, k.inv_k);
-                    hi = pack8_fp8(x + 8, k.inv_k);
+                    lo = pack8_fp8(x, f * k.inv_k);
+                    hi = pack8_fp8(x + 8, f * k.inv_k);
                 }
                 store_fp8_lane(reinterpret_cast<uint8_t*>(row), gl, lm, lo, hi);
             } else {
@@ -451,7 +472,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     preload_kernargs(a);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: cursor math stays scalar
     const int grp = lane / G;        // head-row slot of this lane in the wave
     const int gl = lane % G;         // lane inside the head row
     const LaneMap lm = lane_map<D, PART>(a.rot, gl);
@@ -473,8 +494,24 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
             bhi = (int)((int64_t)a.total_items * (blockIdx.x + 1) / a.grid);
             return blo < bhi;
         }
-        const int64_t tile = blockIdx.x + (int64_t)(range_k++) * a.grid;
         const int64_t span = a.interleave;
+        int64_t tile;
+        if (a.xcd_spans) {
+            // round k covers spans [k grid, k grid + n); the workgroups of
+            // XCD x (blockIdx % 8, the dispatcher's round-robin) take the
+            // contiguous block [n x / 8, n (x + 1) / 8) of them (grid is a
+            // multiple of 8, so every span of a round has a workgroup)
+            const int64_t nsp = (a.total_items + span - 1) / span;
+            const int64_t base = (int64_t)(range_k++) * a.grid;
+            if (base >= nsp) return false;
+            const int64_t n = min((int64_t)a.grid, nsp - base);
+            const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+            const int64_t lo = n * x / 8, hi = n * (x + 1) / 8;
+            if (lo + j >= hi) return false;
+            tile = base + lo + j;
+        } else {
+            tile = blockIdx.x + (int64_t)(range_k++) * a.grid;
+        }
         if (tile * span >= a.total_items) return false;
         blo = (int)(tile * span);
         bhi = (int)min((int64_t)a.total_items, tile * span + span);
@@ -914,6 +951,13 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     const int cpt = a.chunks_per_token;
     const int span_tok = cpt >= 8 ? 4 : min(kMaxTokensPerTile, (48 + cpt - 1) / cpt);
     la.interleave = (a.T >= 8 * (int64_t)la.grid) ? span_tok * cpt : 0;
+    // With the padded Q-scale layout a span writes each head's scales as one
+    // 16-byte piece of a 128-byte line that 8 consecutive spans share.  Giving
+    // consecutive spans to workgroups of one XCD lets its L2 merge the pieces
+    // into whole lines (written bytes then equal the algorithmic ones; the
+    // 15k-token prefill gains about 2 us).  Other layouts keep the plain
+    // round-robin, which measured faster for them in steady state.
+    la.xcd_spans = (la.interleave > 0 && a.stage_q_scale && la.grid % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, PART, STREAM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();
 }

@@ -126,11 +126,17 @@ __device__ __forceinline__ float sat448(float x) {
     return __builtin_fminf(__builtin_fmaxf(x, -kE4M3Max), kE4M3Max);
 }
 
-// four fp32 -> four E4M3 bytes, x0 in the lowest byte
-__device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, float x3) {
-    int r = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(x0), sat448(x1), 0, false);
-    r = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(x2), sat448(x3), r, true);
+// four fp32 -> four E4M3 bytes, x0 in the lowest byte.  The conversion
+// keeps the other half of its destination; the first one starts from x0's
+// own bits (overwritten by the second), so no register has to be zeroed.
+__device__ __forceinline__ uint32_t cvt_fp8x4(float x0, float x1, float x2, float x3) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, __builtin_bit_cast(int, x0), false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, r, true);
     return (uint32_t)r;
+}
+
+__device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, float x3) {
+    return cvt_fp8x4(sat448(x0), sat448(x1), sat448(x2), sat448(x3));
 }
 
 // eight fp32 (multiplied by `scale`) -> eight E4M3 bytes
@@ -138,6 +144,16 @@ __device__ __forceinline__ uint2 pack8_fp8(const float* x, float scale) {
     uint2 r;
     r.x = pack_fp8x4(x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale);
     r.y = pack_fp8x4(x[4] * scale, x[5] * scale, x[6] * scale, x[7] * scale);
+    return r;
+}
+
+// The same without the saturation, for a scale derived from the values'
+// own amax: then |x * scale| <= upper_max (1 + a few ulp) <= 448.0002, which
+// the conversion already rounds to 448 (it returns NaN only above 464).
+__device__ __forceinline__ uint2 pack8_fp8_bounded(const float* x, float scale) {
+    uint2 r;
+    r.x = cvt_fp8x4(x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale);
+    r.y = cvt_fp8x4(x[4] * scale, x[5] * scale, x[6] * scale, x[7] * scale);
     return r;
 }
 
@@ -169,14 +185,30 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Max of non-negative floats (amax values) over a lane group.  For
+// non-negative floats the order of the values is the order of their bit
+// patterns, so the reduction runs on unsigned integers: a float max of a
+// value moved by DPP would first be canonicalised, one more instruction
+// per step.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
     static_assert(G == 4 || G == 8 || G == 16, "lane groups of 4, 8 or 16");
-    v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap1>(v));
-    v = __builtin_fmaxf(v, dpp_f<kDppQuadSwap2>(v));
-    if constexpr (G >= 8) v = __builtin_fmaxf(v, dpp_f<kDppRowHalfMirror>(v));
-    if constexpr (G == 16) v = __builtin_fmaxf(v, dpp_f<kDppRowMirror>(v));
-    return v;
+    uint32_t u = __float_as_uint(v);
+    u = max(u, dpp_u<kDppQuadSwap1>(u));
+    u = max(u, dpp_u<kDppQuadSwap2>(u));
+    if constexpr (G >= 8) u = max(u, dpp_u<kDppRowHalfMirror>(u));
+    if constexpr (G == 16) u = max(u, dpp_u<kDppRowMirror>(u));
+    return __uint_as_float(u);
+}
+
+// max(a, b) of non-negative floats, as above
+__device__ __forceinline__ float max_nonneg(float a, float b) {
+    return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
 }
 
 // ---------------------------------------------------------------------------

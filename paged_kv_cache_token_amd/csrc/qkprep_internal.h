@@ -95,6 +95,7 @@ struct NraDevArgs {
     float* v_scale_out;
     int32_t stream_qkv;                 // 1: qkv is read once (no Q/K written back): streaming loads
     int32_t interleave;                 // items per round-robin span, 0 = one range per workgroup
+    int32_t xcd_spans;                  // spans of a round grouped by XCD (blockIdx % 8)
     int32_t grid;                       // workgroups launched (set by the launcher)
 };
 
