@@ -433,6 +433,27 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
     }
 }
 
+// Completes the paired-row loads of 64-dim heads.  Lanes 8p .. 8p+3 (row
+// 2p, lane gl) loaded v0 = row 2p [8 gl, +8) and v1 = row 2p+1 [24 - 8 gl,
+// +8); lanes 8p+4+k (row 2p+1) loaded v0 = row 2p [56 - 8k, +8) and v1 = row
+// 2p+1 [32 + 8k, +8).  row_half_mirror pairs lane gl of the even row with
+// lane 3 - gl of the odd row, so each side receives exactly the vector it
+// lacks: the odd row's lanes (DPP banks 1 and 3) their first vector, the even
+// row's lanes (banks 0 and 2) their second.
+__device__ __forceinline__ void pair_exchange(uint4& v0, uint4& v1) {
+    uint4 f, g;
+    f.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.x, (int)v1.x, kDppRowHalfMirror, 0xF, 0xA, false);
+    f.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.y, (int)v1.y, kDppRowHalfMirror, 0xF, 0xA, false);
+    f.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.z, (int)v1.z, kDppRowHalfMirror, 0xF, 0xA, false);
+    f.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.w, (int)v1.w, kDppRowHalfMirror, 0xF, 0xA, false);
+    g.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.x, (int)v0.x, kDppRowHalfMirror, 0xF, 0x5, false);
+    g.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.y, (int)v0.y, kDppRowHalfMirror, 0xF, 0x5, false);
+    g.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.z, (int)v0.z, kDppRowHalfMirror, 0xF, 0x5, false);
+    g.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.w, (int)v0.w, kDppRowHalfMirror, 0xF, 0x5, false);
+    v0 = f;
+    v1 = g;
+}
+
 // (token, chunk) cursor over a wave's run of items; chunk c of token t
 // covers head rows [c * RPW, c * RPW + RPW).
 struct Cursor {
@@ -451,6 +472,11 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     constexpr int RPW = 64 / G;      // head rows per wave
     constexpr int U = kBatch;
     constexpr int D4 = D / 4;        // float4 per cos/sin row
+    // 64-dim heads with whole-head rotary: four lanes hold a 128-byte row,
+    // so one load per lane-vector would read only half of each row's line per
+    // instruction (measured ~10 % slower for streaming loads); rows are read
+    // in pairs of whole lines instead
+    constexpr bool kPairRows = D == 64 && !PART;
     typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
 
     // q_indptr [B+1] | seq_lens [B] | page prefix [B+1] | (padded q_scale) staged scales [TPB][Hq]
@@ -528,11 +554,31 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     auto load_batch = [&](uint4 (&buf)[U][2]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const int tt = ld.left > 0 ? ld.t : t_first;
+            const uint16_t* tok = (a.T > 0 ? a.qkv : g_zero_row) + (int64_t)tt * a.qkv_stride;
+            if constexpr (kPairRows) {
+                // rows 2p and 2p+1 of the chunk: the first load reads the whole
+                // line of row 2p (its lanes their first vectors, row 2p+1's
+                // lanes its second vectors, mirrored), the second the whole
+                // line of row 2p+1; pair_exchange then gives every lane its own
+                const int ra = ld.c * RPW + (grp & ~1), rb = ra + 1;
+                const bool even = (grp & 1) == 0;
+                const uint16_t* sa = tok + ((ld.left > 0 && ra < a.R) ? ra : 0) * D + (even ? 8 * gl : 56 - 8 * gl);
+                const uint16_t* sb = tok + ((ld.left > 0 && rb < a.R) ? rb : 0) * D + (even ? 24 - 8 * gl : 32 + 8 * gl);
+                if constexpr (STREAM) {
+                    buf[u][0] = ld16_stream(sa);
+                    buf[u][1] = ld16_stream(sb);
+                } else {
+                    buf[u][0] = ld16(sa);
+                    buf[u][1] = ld16(sb);
+                }
+                ld.advance(CPT);
+                continue;
+            }
             const int r = ld.c * RPW + grp;
             const bool ok = ld.left > 0 && r < a.R;
             const int rr = ok ? r : 0;
-            const int tt = ld.left > 0 ? ld.t : t_first;
-            const uint16_t* src = (a.T > 0 ? a.qkv : g_zero_row) + (int64_t)tt * a.qkv_stride + rr * D;
+            const uint16_t* src = tok + rr * D;
             if constexpr (STREAM) {
                 buf[u][0] = ld16_stream(src + lm.o0);
                 buf[u][1] = ld16_stream(src + lm.o1);
@@ -799,6 +845,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (pr.left > 0) {
+                if constexpr (kPairRows) pair_exchange(buf[u][0], buf[u][1]);   // all lanes active here
                 const int r = pr.c * RPW + grp;
                 const int ti = pr.t - t_first;
                 if (r < a.R && s_pos[ti] >= 0)

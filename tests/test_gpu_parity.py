@@ -196,6 +196,31 @@ def test_head_dim_64_gqa_8_to_1():
     run_and_compare(inp)
 
 
+@pytest.mark.parametrize("hq,hkv,q_mode,kv_fp8,rope", [
+    (3, 1, W.Q_BF16, False, W.ROPE_NEOX),          # 5 rows: the last row pair has one row past the end
+    (7, 1, W.Q_FP8_DYNAMIC, True, W.ROPE_NEOX),    # 9 rows
+    (5, 5, W.Q_FP8_STATIC, True, W.ROPE_INTERLEAVED),   # 15 rows, interleaved pairs
+    (24, 8, W.Q_FP8_DYNAMIC, False, W.ROPE_NEOX),  # 40 rows: chunks of 16 rows end mid-token
+])
+def test_head_dim_64_row_pairs(hq, hkv, q_mode, kv_fp8, rope):
+    """64-dim heads are loaded as pairs of whole 128-byte rows and exchanged
+    between lanes: row counts that leave a pair half past the last row, and
+    chunks that end inside a token, against the oracle."""
+    q, prior = _ragged(640 + hq, B=5, max_q=90, max_prior=300)
+    inp = W.nra_case(seed=640 + hq, q_lens=q, prior_lens=prior, Hq=hq, Hkv=hkv, D=64, page_size=16,
+                     rope=rope, q_mode=q_mode, kv_fp8=kv_fp8, k_scale=0.05, v_scale=0.05)
+    run_and_compare(inp)
+
+
+def test_head_dim_64_long_call_row_pairs():
+    """A 64-dim call long enough for round-robin spans (about 10k tokens),
+    token-major Q scales."""
+    q = np.array([3000, 2500, 2000, 2700], dtype=np.int64)
+    inp = W.nra_case(seed=6464, q_lens=q, prior_lens=np.zeros(4, np.int64), Hq=16, Hkv=2, D=64, page_size=32,
+                     q_mode=W.Q_FP8_DYNAMIC, kv_fp8=True, k_scale=0.05, v_scale=0.05)
+    run_and_compare(inp)
+
+
 @pytest.mark.parametrize("qlen", [127, 128, 129])
 def test_dynamic_scale_padding_edge(qlen):
     """4 requests x Q tokens with max_seqlen = Q: the padded q_scale row is
