@@ -433,23 +433,31 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
     }
 }
 
-// Completes the paired-row loads of 64-dim heads.  Lanes 8p .. 8p+3 (row
-// 2p, lane gl) loaded v0 = row 2p [8 gl, +8) and v1 = row 2p+1 [24 - 8 gl,
-// +8); lanes 8p+4+k (row 2p+1) loaded v0 = row 2p [56 - 8k, +8) and v1 = row
-// 2p+1 [32 + 8k, +8).  row_half_mirror pairs lane gl of the even row with
-// lane 3 - gl of the odd row, so each side receives exactly the vector it
-// lacks: the odd row's lanes (DPP banks 1 and 3) their first vector, the even
-// row's lanes (banks 0 and 2) their second.
-__device__ __forceinline__ void pair_exchange(uint4& v0, uint4& v1) {
+// Completes loads that read whole lines for lanes that do not own them.
+// Each lane loaded v0 and v1; a DPP mirror (CTRL) pairs it with a partner,
+// and lanes in the banks of RECV_FIRST take the partner's v1 as their first
+// vector, lanes in the banks of RECV_SECOND the partner's v0 as their second
+// (DPP banks are the 4-lane groups of each 16-lane row).
+//  - 64-dim heads (row_half_mirror, 0xA / 0x5): lanes 8p .. 8p+3 (row 2p,
+//    lane gl) loaded v0 = row 2p [8 gl, +8) and v1 = row 2p+1 [24 - 8 gl, +8);
+//    lanes 8p+4+k (row 2p+1) loaded v0 = row 2p [56 - 8k, +8) and v1 = row
+//    2p+1 [32 + 8k, +8).
+//  - Rotary over half the head, 8 or 16 lanes per row (row_half_mirror 0xA /
+//    0x5, or row_mirror 0xC / 0x3): rope lane gl (< G/2) loaded v0 = [8 gl,
+//    +8) and v1 = the first vector [16 (G-1-gl), +8) of pass lane G-1-gl; pass
+//    lane gl loaded v0 = the second vector [R/2 + 8 (G-1-gl), +8) of rope lane
+//    G-1-gl and v1 = its own [16 gl + 8, +8).
+template <int CTRL, int RECV_FIRST, int RECV_SECOND>
+__device__ __forceinline__ void mirror_exchange(uint4& v0, uint4& v1) {
     uint4 f, g;
-    f.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.x, (int)v1.x, kDppRowHalfMirror, 0xF, 0xA, false);
-    f.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.y, (int)v1.y, kDppRowHalfMirror, 0xF, 0xA, false);
-    f.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.z, (int)v1.z, kDppRowHalfMirror, 0xF, 0xA, false);
-    f.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.w, (int)v1.w, kDppRowHalfMirror, 0xF, 0xA, false);
-    g.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.x, (int)v0.x, kDppRowHalfMirror, 0xF, 0x5, false);
-    g.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.y, (int)v0.y, kDppRowHalfMirror, 0xF, 0x5, false);
-    g.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.z, (int)v0.z, kDppRowHalfMirror, 0xF, 0x5, false);
-    g.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.w, (int)v0.w, kDppRowHalfMirror, 0xF, 0x5, false);
+    f.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.x, (int)v1.x, CTRL, 0xF, RECV_FIRST, false);
+    f.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.y, (int)v1.y, CTRL, 0xF, RECV_FIRST, false);
+    f.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.z, (int)v1.z, CTRL, 0xF, RECV_FIRST, false);
+    f.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.w, (int)v1.w, CTRL, 0xF, RECV_FIRST, false);
+    g.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.x, (int)v0.x, CTRL, 0xF, RECV_SECOND, false);
+    g.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.y, (int)v0.y, CTRL, 0xF, RECV_SECOND, false);
+    g.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.z, (int)v0.z, CTRL, 0xF, RECV_SECOND, false);
+    g.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.w, (int)v0.w, CTRL, 0xF, RECV_SECOND, false);
     v0 = f;
     v1 = g;
 }
@@ -477,6 +485,10 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     // instruction (measured ~10 % slower for streaming loads); rows are read
     // in pairs of whole lines instead
     constexpr bool kPairRows = D == 64 && !PART;
+    // Rotary over half the head (8 or 16 lanes per row): the rope lanes' and
+    // the pass-through lanes' vectors interleave within each line, so the
+    // loads are rearranged the same way (one instruction per half of the row)
+    const bool half_rot = PART && D >= 128 && 2 * a.rot == D;
     typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
 
     // q_indptr [B+1] | seq_lens [B] | page prefix [B+1] | (padded q_scale) staged scales [TPB][Hq]
@@ -579,6 +591,22 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
             const bool ok = ld.left > 0 && r < a.R;
             const int rr = ok ? r : 0;
             const uint16_t* src = tok + rr * D;
+            if constexpr (PART && D >= 128) {
+                if (half_rot) {
+                    const bool rope_lane = gl < G / 2;
+                    const uint16_t* s0 = src + (rope_lane ? 8 * gl : D / 4 + 8 * (G - 1 - gl));
+                    const uint16_t* s1 = src + (rope_lane ? 16 * (G - 1 - gl) : 16 * gl + 8);
+                    if constexpr (STREAM) {
+                        buf[u][0] = ld16_stream(s0);
+                        buf[u][1] = ld16_stream(s1);
+                    } else {
+                        buf[u][0] = ld16(s0);
+                        buf[u][1] = ld16(s1);
+                    }
+                    ld.advance(CPT);
+                    continue;
+                }
+            }
             if constexpr (STREAM) {
                 buf[u][0] = ld16_stream(src + lm.o0);
                 buf[u][1] = ld16_stream(src + lm.o1);
@@ -845,7 +873,14 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (pr.left > 0) {
-                if constexpr (kPairRows) pair_exchange(buf[u][0], buf[u][1]);   // all lanes active here
+                // (all lanes active here)
+                if constexpr (kPairRows) mirror_exchange<kDppRowHalfMirror, 0xA, 0x5>(buf[u][0], buf[u][1]);
+                if constexpr (PART && D == 128) {
+                    if (half_rot) mirror_exchange<kDppRowHalfMirror, 0xA, 0x5>(buf[u][0], buf[u][1]);
+                }
+                if constexpr (PART && D == 256) {
+                    if (half_rot) mirror_exchange<kDppRowMirror, 0xC, 0x3>(buf[u][0], buf[u][1]);
+                }
                 const int r = pr.c * RPW + grp;
                 const int ti = pr.t - t_first;
                 if (r < a.R && s_pos[ti] >= 0)

@@ -142,6 +142,12 @@ def test_partial_rotary(D, R, arm):
     run_and_compare(inp)
 
 
+def test_partial_rotary_full_size_prefill():
+    """The 15k-token FP8 prefill with rotary over 64 of 128 dims: round-robin
+    spans, and the half-rotary loads that read whole lines."""
+    print(run_and_compare(W.c3_prefill_fp8(rotary_dim=64)), flush=True)
+
+
 # K/V redirect to caller rows (caches untouched, no tail clear) and dynamic
 # FP8 K/V scales per (token, kv head) or per group of dims
 @pytest.mark.parametrize("addressing", [W.ADDR_PAGED, W.ADDR_SLOT])
