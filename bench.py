@@ -225,6 +225,7 @@ class MlaCall:
         sc = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)  # noqa: E731
         self.q_out = None if inp.q_out0 is None else up(inp.q_out0, torch.uint8)
         self.q_scale = None if inp.q_scale0 is None else up(inp.q_scale0, torch.float32)
+        # (the params struct keeps every tensor below alive)
         self.params = qp.mla_params(
             q=self.q, kv_c=up(inp.kv_c, torch.int16), k_pe=up(inp.k_pe, torch.int16),
             cos_sin_cache=up(inp.cos_sin, torch.float32), positions=up(inp.positions, torch.int64),

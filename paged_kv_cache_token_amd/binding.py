@@ -155,8 +155,17 @@ def norm_rope_append_params(*, qkv, num_q_heads, num_kv_heads, head_dim, cos_sin
                             rotary_dim=None, out_k=None, out_v=None, out_kv_row_stride=None,
                             kv_scale_mode=KV_SCALE_STATIC, kv_group_size=0, k_scale_out=None,
                             v_scale_out=None) -> NormRopeAppendParams:
-    """Fill the params struct from tensors (shapes/strides read from them when not given)."""
+    """Fill the params struct from tensors (shapes/strides read from them when not given).
+
+    The struct holds raw device pointers; it also keeps a reference to every
+    tensor it points into, so the memory stays allocated as long as the
+    struct is alive (a temporary passed here would otherwise be freed and its
+    memory handed to the next allocation)."""
     p = NormRopeAppendParams()
+    p._tensors = tuple(t for t in (qkv, cos_sin_cache, positions, k_cache, v_cache, q_out, q_norm_weight,
+                                   k_norm_weight, q_indptr, seq_lens, page_table, slot_mapping, k_scale, v_scale,
+                                   q_scale, q_scale_inv, k_out, flags, out_k, out_v, k_scale_out, v_scale_out)
+                       if t is not None)
     p.num_tokens = qkv.shape[0] if num_tokens is None else num_tokens
     p.num_q_heads, p.num_kv_heads, p.head_dim = num_q_heads, num_kv_heads, head_dim
     p.rotary_dim = head_dim if rotary_dim is None else rotary_dim
@@ -219,7 +228,11 @@ def mla_params(*, q, kv_c, k_pe, cos_sin_cache, positions, slot_mapping, kv_cach
                kv_scale=None, num_tokens=None, q_token_stride=None, q_head_stride=None, q_mode=Q_BF16,
                q_out=None, q_out_token_stride=None, q_out_head_stride=None, q_scale=None, q_scale_inv=None,
                upper_max=448.0) -> MlaParams:
+    """Fill the MLA params struct from tensors; like norm_rope_append_params,
+    the struct keeps a reference to every tensor it points into."""
     p = MlaParams()
+    p._tensors = tuple(t for t in (q, kv_c, k_pe, cos_sin_cache, positions, slot_mapping, kv_cache, kv_scale,
+                                   q_out, q_scale, q_scale_inv) if t is not None)
     p.num_tokens = q.shape[0] if num_tokens is None else num_tokens
     p.num_q_heads, p.nope_dim, p.rope_dim, p.kv_lora_rank = num_q_heads, nope_dim, rope_dim, kv_lora_rank
     p.q = _ptr(q)

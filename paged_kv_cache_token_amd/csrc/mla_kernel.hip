@@ -94,9 +94,16 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     preload_kernargs(a);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int grp = lane / kLanesPerHead;
     const int gl = lane % kLanesPerHead;
+    // element offsets (in the rope slice) of the two whole-line loads and
+    // stores of head pair (2p, 2p+1): the even head's lanes read their own
+    // first vector and the odd head's lanes the even head's second vector,
+    // then the odd head's line the same way
+    const bool even_head = (grp & 1) == 0;
+    const int q_off0 = even_head ? 8 * gl : 56 - 8 * gl;
+    const int q_off1 = even_head ? 24 - 8 * gl : 32 + 8 * gl;
     const int K = a.kv_lora_rank;
     const int row_len = K + kRope;
     const int CPT = a.chunks_per_token;
@@ -122,10 +129,12 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
             const uint16_t* p0;
             const uint16_t* p1;
             if (ld.c < n_qchunks) {
-                const int h0 = ld.c * kHeadsPerWave + grp;
-                const int h = h0 < a.H ? h0 : 0;
-                p0 = a.q + (int64_t)t * a.q_token_stride + (int64_t)h * a.q_head_stride + a.nope_dim + 8 * gl;
-                p1 = p0 + kHalf;
+                // heads 2p and 2p+1 of the chunk: each load reads one head's
+                // whole 128-byte rope slice (mirror_exchange completes them)
+                const int ha = ld.c * kHeadsPerWave + (grp & ~1), hb = ha + 1;
+                const uint16_t* q = a.q + (int64_t)t * a.q_token_stride + a.nope_dim;
+                p0 = q + (int64_t)(ha < a.H ? ha : 0) * a.q_head_stride + q_off0;
+                p1 = q + (int64_t)(hb < a.H ? hb : 0) * a.q_head_stride + q_off1;
             } else {
                 p0 = a.kv_c + (int64_t)t * a.kv_c_stride + 8 * lane;
                 p1 = a.k_pe + (int64_t)t * a.k_pe_stride + 8 * (lane & 7);
@@ -181,18 +190,21 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
                 const int chunk = pr.c;
                 const int pos = s_pos[ti];
                 if (chunk < n_qchunks) {
-                    const int h = chunk * kHeadsPerWave + grp;
-                    if (pos >= 0 && h < a.H) {
-                        float c[8], s[8], x[16];
-                        lane_cos_sin(s_cs + ti * kRope, gl, a.rope, c, s);
-                        unpack8(buf[u][0], x);
-                        unpack8(buf[u][1], x + 8);
-                        rope16(x, c, s, a.rope);
-                        uint16_t* p = a.q + (int64_t)t * a.q_token_stride + (int64_t)h * a.q_head_stride +
-                                      a.nope_dim + 8 * gl;
-                        st16(p, pack8_bf16(x));
-                        st16(p + kHalf, pack8_bf16(x + 8));
-                    }
+                    // (wave-uniform branch: every lane takes part in the exchanges)
+                    mirror_exchange<kDppRowHalfMirror, 0xA, 0x5>(buf[u][0], buf[u][1]);
+                    float c[8], s[8], x[16];
+                    lane_cos_sin(s_cs + ti * kRope, gl, a.rope, c, s);
+                    unpack8(buf[u][0], x);
+                    unpack8(buf[u][1], x + 8);
+                    rope16(x, c, s, a.rope);
+                    uint4 lo = pack8_bf16(x), hi = pack8_bf16(x + 8);
+                    // the same exchange turns the lane's own halves into the
+                    // whole-line stores at the load addresses
+                    mirror_exchange<kDppRowHalfMirror, 0xA, 0x5>(lo, hi);
+                    const int ha = chunk * kHeadsPerWave + (grp & ~1), hb = ha + 1;
+                    uint16_t* q = a.q + (int64_t)t * a.q_token_stride + a.nope_dim;
+                    if (pos >= 0 && ha < a.H) st16(q + (int64_t)ha * a.q_head_stride + q_off0, lo);
+                    if (pos >= 0 && hb < a.H) st16(q + (int64_t)hb * a.q_head_stride + q_off1, hi);
                 } else {
                     // k_pe second halves come from lanes 4..7 (all lanes take part)
                     const uint4 pe = buf[u][1];
@@ -313,7 +325,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
     preload_kernargs(a);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int grp = lane / kLanesPerHead;
     const int gl = lane % kLanesPerHead;
     const int N = a.nope_dim;
@@ -350,9 +362,11 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                 const int h = (r0 + k) * 64 + wave * kHeadsPerWave + grp;
                 hh[k] = h;
                 const uint16_t* qh = qt + (int64_t)(h < a.H ? h : 0) * a.q_head_stride;
-#pragma unroll
                 // nope vector j of lane gl: elements [8 (gl + 4 j), +8), so that
                 // each load instruction reads 64 contiguous bytes of a head
+                // (loading head pairs one whole line per instruction, as the
+                // in-place kernel does, measured no faster here)
+#pragma unroll
                 for (int j = 0; j < 4; ++j) vn[k][j] = j < NV ? ld16(qh + 8 * (gl + 4 * j)) : make_uint4(0, 0, 0, 0);
                 vr[k][0] = ld16(qh + N + 8 * gl);
                 vr[k][1] = ld16(qh + N + kHalf + 8 * gl);

@@ -211,6 +211,40 @@ __device__ __forceinline__ float max_nonneg(float a, float b) {
     return __uint_as_float(max(__float_as_uint(a), __float_as_uint(b)));
 }
 
+// Whole-line loads for lanes that do not own the whole line.  When four
+// lanes hold a 128-byte row as two 16-byte vectors each, a load instruction
+// in which every lane reads its own vector covers only half of each row's
+// line.  Rows are then loaded in pairs, one whole line per instruction, and
+// this exchange completes them.  Each lane loaded v0 and v1; a DPP mirror
+// (CTRL) pairs it with a partner,
+// and lanes in the banks of RECV_FIRST take the partner's v1 as their first
+// vector, lanes in the banks of RECV_SECOND the partner's v0 as their second
+// (DPP banks are the 4-lane groups of each 16-lane row).
+//  - Four lanes per 128-byte row (row_half_mirror, 0xA / 0x5), elements
+//    [8 gl, +8) and [32 + 8 gl, +8) of the row per lane: lanes 8p .. 8p+3 (row 2p,
+//    lane gl) loaded v0 = row 2p [8 gl, +8) and v1 = row 2p+1 [24 - 8 gl, +8);
+//    lanes 8p+4+k (row 2p+1) loaded v0 = row 2p [56 - 8k, +8) and v1 = row
+//    2p+1 [32 + 8k, +8).
+//  - Rotary over half the head, 8 or 16 lanes per row (row_half_mirror 0xA /
+//    0x5, or row_mirror 0xC / 0x3): rope lane gl (< G/2) loaded v0 = [8 gl,
+//    +8) and v1 = the first vector [16 (G-1-gl), +8) of pass lane G-1-gl; pass
+//    lane gl loaded v0 = the second vector [R/2 + 8 (G-1-gl), +8) of rope lane
+//    G-1-gl and v1 = its own [16 gl + 8, +8).
+template <int CTRL, int RECV_FIRST, int RECV_SECOND>
+__device__ __forceinline__ void mirror_exchange(uint4& v0, uint4& v1) {
+    uint4 f, g;
+    f.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.x, (int)v1.x, CTRL, 0xF, RECV_FIRST, false);
+    f.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.y, (int)v1.y, CTRL, 0xF, RECV_FIRST, false);
+    f.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.z, (int)v1.z, CTRL, 0xF, RECV_FIRST, false);
+    f.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.w, (int)v1.w, CTRL, 0xF, RECV_FIRST, false);
+    g.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.x, (int)v0.x, CTRL, 0xF, RECV_SECOND, false);
+    g.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.y, (int)v0.y, CTRL, 0xF, RECV_SECOND, false);
+    g.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.z, (int)v0.z, CTRL, 0xF, RECV_SECOND, false);
+    g.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.w, (int)v0.w, CTRL, 0xF, RECV_SECOND, false);
+    v0 = f;
+    v1 = g;
+}
+
 // ---------------------------------------------------------------------------
 // wave and block primitives
 // ---------------------------------------------------------------------------

@@ -180,3 +180,37 @@ def test_status_strings():
     for s in range(8):
         assert qp.qkprep_status_string(s)
     assert "unknown" in qp.qkprep_status_string(99)
+
+
+def test_params_keep_their_tensors_alive():
+    """The structs hold raw pointers; they must also hold the tensors, or a
+    temporary passed in is freed and its memory reused by the next allocation."""
+    import gc
+    import weakref
+    import torch
+
+    class T(torch.Tensor):
+        pass
+
+    def mk(n, dt=torch.float32):
+        return torch.zeros(n, dtype=dt).as_subclass(T)
+
+    kv_c = mk((4, 512), torch.int16)
+    ref = weakref.ref(kv_c)
+    p = B.mla_params(q=mk((4, 128, 192), torch.int16), kv_c=kv_c, k_pe=mk((4, 64), torch.int16),
+                     cos_sin_cache=mk((16, 64)), positions=mk(4, torch.int64), slot_mapping=mk(4, torch.int64),
+                     kv_cache=mk((4, 64, 576), torch.uint8), num_q_heads=128, kv_scale=mk(1))
+    del kv_c
+    gc.collect()
+    assert ref() is not None and p.kv_c == ref().data_ptr()
+    w = mk(128)
+    wref = weakref.ref(w)
+    p2 = B.norm_rope_append_params(qkv=mk((4, 1280), torch.int16), num_q_heads=8, num_kv_heads=1, head_dim=128,
+                                   cos_sin_cache=mk((16, 128)), positions=mk(4, torch.int64),
+                                   k_cache=mk((8, 16, 1, 128), torch.int16), v_cache=mk((8, 16, 1, 128), torch.int16),
+                                   q_out=mk((4, 1024), torch.int16), q_norm_weight=w, k_norm_weight=mk(128),
+                                   q_indptr=mk(2, torch.int32), seq_lens=mk(1, torch.int32),
+                                   page_table=mk((1, 8), torch.int32), flags=mk(1, torch.int32))
+    del w
+    gc.collect()
+    assert wref() is not None and p2.q_norm_weight == wref().data_ptr()

@@ -418,7 +418,7 @@ def test_requests_spread_tails_with_scattered_page_slots():
 
 @pytest.mark.parametrize("fp8", [True, False])
 @pytest.mark.parametrize("rope", [W.ROPE_INTERLEAVED, W.ROPE_NEOX])
-@pytest.mark.parametrize("H_", [128, 16, 20])
+@pytest.mark.parametrize("H_", [128, 16, 20, 7, 1])   # odd H: the last head pair has one head past H
 def test_mla_variants(fp8, rope, H_):
     inp = W.mla_case(seed=H_ + rope, T=77, H=H_, num_blocks=8, block_size=16, kv_fp8=fp8, rope=rope,
                      negative_slots=3)
@@ -450,7 +450,8 @@ def test_mla_fp8_q_full_size(q_mode):
 # nope_dim multiple of 32 up to 128 (odd nope-vector counts store 8-byte
 # pieces), head counts below, at and above a 64-head round, both caches
 @pytest.mark.parametrize("q_mode", [W.Q_FP8_DYNAMIC, W.Q_FP8_STATIC])
-@pytest.mark.parametrize("H_,nope", [(128, 128), (16, 64), (20, 96), (100, 32), (3, 0), (64, 128)])
+@pytest.mark.parametrize("H_,nope", [(128, 128), (16, 64), (20, 96), (100, 32), (3, 0), (64, 128), (7, 64),
+                                     (1, 128)])
 @pytest.mark.parametrize("fp8", [True, False])
 def test_mla_fp8_q_variants(q_mode, H_, nope, fp8):
     inp = W.mla_case(seed=H_ + nope + q_mode, T=61, H=H_, nope_dim=nope, num_blocks=8, block_size=16,
