@@ -320,9 +320,7 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
     // apply it here.
     float f = 1.0f;
     if (a.norm != 0) {
-        float ss = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ss = fmaf(x[i], x[i], ss);
+        float ss = sumsq8_bf16(v1, sumsq8_bf16(v0, 0.0f));
         ss = group_sum<G>(ss);
         // the argument is >= eps > 0; the floor keeps v_rsq off denormal
         // inputs (an all-zero row with eps < 2^-126 stays zero)

@@ -94,6 +94,19 @@ __device__ __forceinline__ int fdiv31(int n, const FD& f) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Sum of squares of the 8 bf16 values of a 16-byte vector, added to acc:
+// v_dot2_f32_bf16 squares a packed bf16 pair (exact in fp32) and accumulates
+// in fp32, so the unpacked values are not needed for it.
+__device__ __forceinline__ float sumsq8_bf16(uint4 v, float acc) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2_t p = __builtin_bit_cast(bf16x2_t, w[i]);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+    }
+    return acc;
+}
+
 // 8 bf16 values of a 16-byte vector -> fp32 x[0..7]
 __device__ __forceinline__ void unpack8(uint4 v, float* x) {
     x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
