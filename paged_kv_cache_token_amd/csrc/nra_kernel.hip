@@ -875,8 +875,8 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
         const uint4 z = make_uint4(0, 0, 0, 0);
         const int64_t v1 = nvec * (slice + 1) / nslices;
         for (int64_t i = nvec * slice / nslices + tid; i < v1; i += kBlockThreads) {
-            st16(kb + 16 * i, z);
-            st16(vb + 16 * i, z);
+            st16_stream(kb + 16 * i, z);
+            st16_stream(vb + 16 * i, z);
         }
         if (kc.kv_ng) {
             // the cleared rows' dynamic scales

@@ -55,6 +55,15 @@ __device__ __forceinline__ void st16(void* p, uint4 v) {
     *reinterpret_cast<uint4*>(p) = v;
 }
 
+// Streaming store (non-temporal hint): for data no kernel reads soon (the
+// zeroed tail rows), so that it drains to memory during the kernel instead
+// of staying dirty in the caches until the end-of-kernel write-back.
+__device__ __forceinline__ void st16_stream(void* p, uint4 v) {
+    typedef __attribute__((address_space(1))) u32x4_t gT;
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (gT*)p);
+}
+
 __device__ __forceinline__ void st8(void* p, uint2 v) {
     *reinterpret_cast<uint2*>(p) = v;
 }
