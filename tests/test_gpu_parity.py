@@ -365,6 +365,31 @@ def test_malformed_metadata(mutation):
     assert (ref["flags"] == -1).all()
 
 
+@pytest.mark.parametrize("b", [5, 550])
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_out_of_pool_page_in_each_check_path(b, which):
+    """600 requests writing 3-4 pages each (more than the 512 requests whose
+    metadata the prologue holds in registers, more pages than the 256 page
+    slots): a page id past the pool as a request's 1st, 2nd or 3rd written
+    page, for a request below and one above 512, must reject the whole call."""
+    B = 600
+    q = np.full(B, 12, dtype=np.int64)
+    prior = np.arange(B, dtype=np.int64) % 4
+    inp = W.nra_case(seed=600 + b + which, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=4,
+                     maxp=8)
+    first = int(prior[b]) // 4
+    inp.page_table[b, first + which] = inp.num_pages + 1
+    dev = H.DeviceNra(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    gpu = dev.host_outputs()
+    assert (gpu["flags"] == -1).all()
+    H.check_exact(gpu["k_cache"], inp.k_cache0, "k_cache")
+    H.check_exact(gpu["v_cache"], inp.v_cache0, "v_cache")
+    assert (H.oracle_outputs(inp)["flags"] == -1).all()
+
+
 def test_many_requests_cross_page_ragged():
     rng = np.random.default_rng(99)
     B = 300
