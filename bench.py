@@ -63,6 +63,8 @@ def parse():
                     help="time every workload (the five configurations and the variant rows) one by one "
                          "and print one JSON object; no headline line")
     ap.add_argument("--suite-only", default=None, help="comma-separated subset of the suite's workloads")
+    ap.add_argument("--suite-launches", type=int, default=200,
+                    help="clean-cache launches per session (three sessions) of each suite workload")
     return ap.parse_args()
 
 
@@ -75,6 +77,7 @@ def suite_workloads():
     return {
         "c1_tiny_decode": (W.c1_tiny_decode, "nra"),
         "c2_decode_b256": (W.c2_decode_b256, "nra"),
+        "c2_decode_b256_no_tail_clear": (lambda: W.c2_decode_b256(zero_tail=False), "nra"),
         "c3_prefill_fp8": (W.c3_prefill_fp8, "nra"),
         "c4_strided_d256": (W.c4_strided_d256, "nra"),
         "c5_mla": (W.c5_mla, "mla"),
@@ -91,10 +94,22 @@ def suite_workloads():
     }
 
 
+def percentile(sorted_vals, q):
+    """q-quantile (0..1) of an ascending list, by linear interpolation."""
+    if not sorted_vals:
+        return None
+    x = q * (len(sorted_vals) - 1)
+    i = int(x)
+    j = min(i + 1, len(sorted_vals) - 1)
+    return sorted_vals[i] + (sorted_vals[j] - sorted_vals[i]) * (x - i)
+
+
 def run_suite(args, dev):
-    """Each workload alone: the average of 20 back-to-back launches (events
-    on the launch stream around each) and the median of 15 launches after a
-    clean 512 MiB read flush."""
+    """Each workload alone: 20 warm-up launches; three runs of 20
+    back-to-back launches (events on the launch stream around each run);
+    then three sessions of --suite-launches launches, each after a clean
+    512 MiB read flush of L2 and the Infinity Cache (events around each
+    launch): median, p10 and p90 over all of them and each session's median."""
     import torch
     table = {}
     names = list(suite_workloads())
@@ -102,36 +117,48 @@ def run_suite(args, dev):
         names = [n for n in args.suite_only.split(",") if n]
     stream = torch.cuda.current_stream()
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    n_clean = args.suite_launches
     for name in names:
         make, kind = suite_workloads()[name]
         log(f"suite: {name}")
         inp = make()
         c = MlaCall(inp, dev) if kind == "mla" else Call(inp, dev)
+        for _ in range(20):
+            c.launch()
+        torch.cuda.synchronize()
+        runs = []
         for _ in range(3):
-            c.launch()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
-        ev[0].record(stream)
-        for k in range(20):
-            c.launch()
-            ev[k + 1].record(stream)
-        torch.cuda.synchronize()
-        warm = [ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(20)]
-        cold = []
-        for _ in range(15):
-            flush.sum()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            c.launch()
+            for _ in range(20):
+                c.launch()
             e1.record(stream)
             torch.cuda.synchronize()
-            cold.append(e0.elapsed_time(e1) * 1e3)
-        cold.sort()
-        avg = sum(warm) / len(warm)
-        med = cold[len(cold) // 2]
+            runs.append(e0.elapsed_time(e1) * 1e3 / 20)
+        sessions = []
+        for _ in range(3):
+            cold = []
+            for _ in range(n_clean):
+                flush.sum()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                c.launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1) * 1e3)
+            sessions.append(sorted(cold))
+        allc = sorted(x for ses in sessions for x in ses)
+        avg = sorted(runs)[1]
+        med = percentile(allc, 0.5)
         table[name] = {"tokens": inp.T, "algorithmic_bytes": c.bytes, "avg_us": round(avg, 2),
+                       "back_to_back_runs_us": [round(r, 2) for r in runs],
                        "clean_cache_median_us": round(med, 2),
+                       "clean_cache_p10_us": round(percentile(allc, 0.1), 2),
+                       "clean_cache_p90_us": round(percentile(allc, 0.9), 2),
+                       "clean_cache_session_medians_us": [round(percentile(ses, 0.5), 2) for ses in sessions],
+                       "clean_cache_launches": len(allc),
                        "GBps": round(c.bytes / (avg * 1e-6) / 1e9, 1),
                        "clean_cache_GBps": round(c.bytes / (med * 1e-6) / 1e9, 1),
                        "clean_cache_pct_of_peak": round(100 * c.bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
@@ -190,7 +217,7 @@ class Call:
             q_indptr=up(inp.q_indptr, torch.int32), seq_lens=up(inp.seq_lens, torch.int32),
             page_table=up(inp.page_table, torch.int32), k_cache=self.k_cache, v_cache=self.v_cache,
             kv_dtype=qp.FP8_E4M3 if inp.kv_fp8 else qp.BF16, k_scale=sc(inp.k_scale), v_scale=sc(inp.v_scale),
-            zero_tail=1, q_out=self.q_out, q_out_row_stride=inp.qkv_row_stride if inp.q_in_place else inp.Hq * inp.D,
+            zero_tail=1 if inp.zero_tail else 0, q_out=self.q_out, q_out_row_stride=inp.qkv_row_stride if inp.q_in_place else inp.Hq * inp.D,
             q_mode=inp.q_mode, k_out=k_out, k_out_row_stride=inp.qkv_row_stride, qkv_row_stride=inp.qkv_row_stride,
             q_scale_inv=sc(inp.q_scale_inv), num_tokens=inp.T,
             q_scale=self.q_scale,
@@ -273,9 +300,40 @@ def recorded_traffic(kernel_hash: str):
         return None
 
 
+def host_cpu():
+    """CPU model name and logical core count of the host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
 def cpu_baseline(c2, c3):
     """The oracle (single-threaded C, fp64) on the same step: the decode call
-    on its touched pages and the full prefill call."""
+    on its touched pages and the full prefill call.  The step is timed three
+    times (once if a run takes over 10 s) and the median reported."""
+    runs = []
+    while True:
+        t, nbytes, ntok = cpu_step(c2, c3)
+        runs.append(t)
+        if len(runs) == 3 or t > 10.0:
+            break
+    t_total = sorted(runs)[len(runs) // 2]
+    model, ncpu = host_cpu()
+    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": round(ntok / t_total, 1), "seconds": round(t_total, 3),
+            "runs_s": [round(r, 3) for r in runs], "host_cpu": model, "host_logical_cores": ncpu,
+            "sample": "one full step (decode B=256 on its touched pages + the ragged FP8 prefill call), "
+                      "single-threaded C oracle in fp64, median of the runs"}
+
+
+def cpu_step(c2, c3):
     import numpy as np
     import oracle
     t_total = 0.0
@@ -307,10 +365,7 @@ def cpu_baseline(c2, c3):
         t_total += time.perf_counter() - t0
         nbytes += call.bytes
         ntok += inp.T
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "tokens_per_s": round(ntok / t_total, 1), "seconds": round(t_total, 3),
-            "sample": "one full step (decode B=256 on its touched pages + the ragged FP8 prefill call), "
-                      "single-threaded C oracle in fp64"}
+    return t_total, nbytes, ntok
 
 
 def copy_calibration(dev):
@@ -420,8 +475,10 @@ def main():
                 torch.cuda.synchronize()
                 durs.append(e0.elapsed_time(e1) * 1e3)
             durs.sort()
-            med = durs[len(durs) // 2]
+            med = percentile(durs, 0.5)
             breakdown[name]["clean_cache_median_us"] = round(med, 2)
+            breakdown[name]["clean_cache_p10_us"] = round(percentile(durs, 0.1), 2)
+            breakdown[name]["clean_cache_p90_us"] = round(percentile(durs, 0.9), 2)
             breakdown[name]["clean_cache_GBps"] = round(c.bytes / (med * 1e-6) / 1e9, 1)
         del flush
     dominant = max(names, key=lambda n: breakdown[n]["avg_us"])
