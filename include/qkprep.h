@@ -59,7 +59,7 @@ typedef enum {
     QKPREP_OK = 0,
     QKPREP_E_NULL = 1,         /* a required pointer is NULL */
     QKPREP_E_SHAPE = 2,        /* inconsistent sizes or strides */
-    QKPREP_E_UNSUPPORTED = 3,  /* a valid configuration this build does not implement */
+    QKPREP_E_UNSUPPORTED = 3,  /* a valid configuration the library does not implement */
     QKPREP_E_ALIGN = 4,        /* a vector-accessed base or stride is not 16-byte aligned */
     QKPREP_E_RANGE = 5,        /* a scalar outside its documented range */
     QKPREP_E_LAUNCH = 6,       /* the HIP launch itself failed */

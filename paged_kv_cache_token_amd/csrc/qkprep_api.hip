@@ -26,7 +26,7 @@ const char* qkprep_status_string(qkprep_status status) {
         case QKPREP_OK: return "ok";
         case QKPREP_E_NULL: return "a required pointer is NULL";
         case QKPREP_E_SHAPE: return "inconsistent sizes or strides";
-        case QKPREP_E_UNSUPPORTED: return "configuration not supported by this build";
+        case QKPREP_E_UNSUPPORTED: return "configuration not supported by this library";
         case QKPREP_E_ALIGN: return "a vector-accessed base address or stride is not 16-byte aligned";
         case QKPREP_E_RANGE: return "a scalar argument is outside its documented range";
         case QKPREP_E_LAUNCH: return "the HIP kernel launch failed";
