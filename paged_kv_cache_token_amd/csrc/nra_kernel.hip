@@ -986,7 +986,13 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     // enough workgroups to fill every CU, none with less than 8 head-row
     // chunks of work, and at least one per 4 requests for the tail clears
     const int64_t cap = resident_blocks<D, QMODE, KVFP8, PART, STREAM>(lds);
+    // 8 (token, chunk) items per workgroup, but 4 for small calls (up to 64
+    // workgroups): a tiny decode's time is its latency chain, which more
+    // workgroups shorten (16 tokens: 9.4 -> 8.1 us), while at B = 256 the
+    // 8-item split measured best
     int64_t want = (a.total_items + 7) / 8;
+    const int64_t want4 = (a.total_items + 3) / 4;
+    if (want < (want4 < 64 ? want4 : 64)) want = want4 < 64 ? want4 : 64;
     if (want < (a.B + 3) / 4) want = (a.B + 3) / 4;
     if (want < 1) want = 1;
     NraDevArgs la = a;
