@@ -19,13 +19,19 @@
 //    covers 64/G head rows of one token (a "chunk").
 //  * The sum of squares and the FP8 amax are reduced over the G lanes of the
 //    row only (DPP within the lane group), never across rows or tokens.
-//  * Every workgroup owns a balanced, contiguous range of the (token, chunk)
-//    items and of the requests; the grid is sized to what stays resident.
-//    Tiles of up to 16 tokens stage their cos/sin rows, positions and cache
-//    row offsets in LDS; the norm weights are staged once per workgroup.
+//  * Short calls give every workgroup a balanced, contiguous range of the
+//    (token, chunk) items; long calls deal spans of tokens round-robin, so
+//    the resident workgroups stream through one window of qkv at a time
+//    (grouped by XCD when the padded Q-scale layout is written).  Every
+//    workgroup also owns a range of the requests; the grid is sized to what
+//    stays resident.  Tiles of up to 16 tokens stage their cos/sin rows,
+//    positions and cache row offsets in LDS; the norm weights are staged
+//    once per workgroup.
 //  * Loads are double-buffered and unconditional (rows past the run are
 //    clamped to a valid row) so that the wait for one batch never drains the
-//    loads of the next one.
+//    loads of the next one.  Where one row's 128-byte line is split between
+//    lanes (64-dim heads, rotary over half the head), rows are loaded one
+//    whole line per instruction and completed by a DPP mirror exchange.
 //  * All-or-nothing validation without a host sync or a second kernel:
 //    every workgroup stages q_indptr / seq_lens in LDS, checks every request
 //    and every page id the call will write (the pages are enumerated through
