@@ -182,8 +182,10 @@ template <int D, bool PART>
 __device__ __forceinline__ LaneMap lane_map(int rot, int gl) {
     LaneMap m;
     if constexpr (!PART) {
-        // whole head rotates: compile-time split, immediate store offsets
-        m.rope = true;
+        // whole head rotates (or, with rot = 0, nothing does: the layout then
+        // only has to be the same for loads and stores): compile-time split,
+        // immediate store offsets
+        m.rope = rot != 0;
         m.o0 = 8 * gl;
         m.o1 = D / 2 + 8 * gl;
         m.hr = D / 2;
@@ -1035,13 +1037,14 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
 
 // Launch for head dim QKPREP_NRA_HEAD_DIM: picks the instance for the Q mode,
 // the cache dtype, whole-head or partial rotary, and streaming or cached
-// qkv loads.
+// qkv loads.  A call without rotated dims takes the whole-head layout, whose
+// load instructions read whole lines.
 hipError_t QKPREP_CAT(launch_norm_rope_append_d, QKPREP_NRA_HEAD_DIM)(const NraDevArgs& a, int q_mode, int kv_fp8,
                                                                        hipStream_t stream) {
     constexpr int D = QKPREP_NRA_HEAD_DIM;
 #define QKPREP_NRA_CASE(QM, KF)                                                                          \
     if (q_mode == QM && (kv_fp8 != 0) == KF) {                                                           \
-        if (a.rot == D)                                                                                  \
+        if (a.rot == D || a.rot == 0)                                                                    \
             return a.stream_qkv ? launch_t<D, QM, KF, false, true>(a, stream)                             \
                                 : launch_t<D, QM, KF, false, false>(a, stream);                           \
         return a.stream_qkv ? launch_t<D, QM, KF, true, true>(a, stream)                                  \

@@ -61,7 +61,9 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
         if (p->kv_scale_mode == QKPREP_KV_SCALE_GROUP) {
             const int g = p->kv_group_size;
             if (g < 8 || (g & (g - 1)) || (g > D / 2 && g != D)) return QKPREP_E_UNSUPPORTED;
-            if (g != D && rot != D) return QKPREP_E_UNSUPPORTED;
+            // groups inside a head need the whole-head lane layout, which
+            // calls rotating all dims or none use
+            if (g != D && rot != D && rot != 0) return QKPREP_E_UNSUPPORTED;
             kv_group = g;
         }
     }

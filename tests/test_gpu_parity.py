@@ -142,6 +142,23 @@ def test_partial_rotary(D, R, arm):
     run_and_compare(inp)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_nope_layer_with_group_kv_scales(D):
+    """No rotated dims (a NoPE layer) takes the whole-head lane layout, so
+    per-group K/V scales smaller than the head are supported there too."""
+    q, prior = _ragged(D + 3, B=5, max_q=30, max_prior=200)
+    inp = W.nra_case(seed=D + 3, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=D, page_size=16, rotary_dim=0,
+                     kv_fp8=True, kv_scale_mode=W.KV_SCALE_GROUP, kv_group_size=32, q_mode=W.Q_FP8_DYNAMIC)
+    inp.positions = inp.positions.copy()
+    inp.positions[:2] = -5          # not read without rotated dims
+    run_and_compare(inp)
+
+
+def test_nope_layer_full_size_prefill():
+    """The 15k-token FP8 prefill of a NoPE layer (rotary_dim = 0)."""
+    print(run_and_compare(W.c3_prefill_fp8(rotary_dim=0)), flush=True)
+
+
 def test_partial_rotary_full_size_prefill():
     """The 15k-token FP8 prefill with rotary over 64 of 128 dims: round-robin
     spans, and the half-rotary loads that read whole lines."""
