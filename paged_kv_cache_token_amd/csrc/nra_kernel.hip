@@ -462,10 +462,13 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     // instruction (measured ~10 % slower for streaming loads); rows are read
     // in pairs of whole lines instead
     constexpr bool kPairRows = D == 64 && !PART;
-    // Rotary over half the head (8 or 16 lanes per row): the rope lanes' and
-    // the pass-through lanes' vectors interleave within each line, so the
-    // loads are rearranged the same way (one instruction per half of the row)
-    const bool half_rot = PART && D >= 128 && 2 * a.rot == D;
+    // Rotary over at most half the head (8 or 16 lanes per row): lanes
+    // 0 .. G/2-1 then hold exactly the first half of the row, but the rope
+    // lanes' two vectors lie R/2 apart, so one load instruction would touch
+    // both lines of a row partly; each lane instead loads its first-half
+    // vector and its mirror partner's (or the partner's and its own
+    // second-half one), and a mirror exchange hands every lane its own
+    const bool half_rot = PART && D >= 128 && 2 * a.rot <= D;
     typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
 
     // q_indptr [B+1] | seq_lens [B] | page prefix [B+1] | (padded q_scale) staged scales [TPB][Hq]
@@ -491,6 +494,14 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     const int grp = lane / G;        // head-row slot of this lane in the wave
     const int gl = lane % G;         // lane inside the head row
     const LaneMap lm = lane_map<D, PART>(a.rot, gl);
+    int ld_o0 = lm.o0, ld_o1 = lm.o1;   // element offsets this lane loads
+    if constexpr (PART && D >= 128) {
+        if (half_rot) {
+            const LaneMap pm = lane_map<D, PART>(a.rot, G - 1 - gl);
+            ld_o0 = gl < G / 2 ? lm.o0 : pm.o1;
+            ld_o1 = gl < G / 2 ? pm.o0 : lm.o1;
+        }
+    }
     int* s_indptr = s_dyn;
     int* s_seqlen = s_dyn + (a.B + 1);
     int* s_pre = s_dyn + (2 * a.B + 1);
@@ -568,28 +579,12 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
             const bool ok = ld.left > 0 && r < a.R;
             const int rr = ok ? r : 0;
             const uint16_t* src = tok + rr * D;
-            if constexpr (PART && D >= 128) {
-                if (half_rot) {
-                    const bool rope_lane = gl < G / 2;
-                    const uint16_t* s0 = src + (rope_lane ? 8 * gl : D / 4 + 8 * (G - 1 - gl));
-                    const uint16_t* s1 = src + (rope_lane ? 16 * (G - 1 - gl) : 16 * gl + 8);
-                    if constexpr (STREAM) {
-                        buf[u][0] = ld16_stream(s0);
-                        buf[u][1] = ld16_stream(s1);
-                    } else {
-                        buf[u][0] = ld16(s0);
-                        buf[u][1] = ld16(s1);
-                    }
-                    ld.advance(CPT);
-                    continue;
-                }
-            }
             if constexpr (STREAM) {
-                buf[u][0] = ld16_stream(src + lm.o0);
-                buf[u][1] = ld16_stream(src + lm.o1);
+                buf[u][0] = ld16_stream(src + ld_o0);
+                buf[u][1] = ld16_stream(src + ld_o1);
             } else {
-                buf[u][0] = ld16(src + lm.o0);
-                buf[u][1] = ld16(src + lm.o1);
+                buf[u][0] = ld16(src + ld_o0);
+                buf[u][1] = ld16(src + ld_o1);
             }
             ld.advance(CPT);
         }
