@@ -178,14 +178,17 @@ struct LaneMap {
     bool rope;
 };
 
-template <int D, bool PART>
+// Rotary layouts, one kernel instance each: the whole head rotates (R = D),
+// its first R dims do (0 < R < D), or none do (R = 0; the whole-head layout,
+// which only has to be the same for loads and stores, with RoPE compiled out)
+enum : int { kRotWhole = 0, kRotPart = 1, kRotNone = 2 };
+
+template <int D, int ROT>
 __device__ __forceinline__ LaneMap lane_map(int rot, int gl) {
     LaneMap m;
-    if constexpr (!PART) {
-        // whole head rotates (or, with rot = 0, nothing does: the layout then
-        // only has to be the same for loads and stores): compile-time split,
-        // immediate store offsets
-        m.rope = rot != 0;
+    if constexpr (ROT != kRotPart) {
+        // compile-time split, immediate store offsets
+        m.rope = ROT == kRotWhole;
         m.o0 = 8 * gl;
         m.o1 = D / 2 + 8 * gl;
         m.hr = D / 2;
@@ -451,13 +454,14 @@ struct Cursor {
     }
 };
 
-template <int D, int QMODE, bool KVFP8, bool PART, bool STREAM>
+template <int D, int QMODE, bool KVFP8, int ROT, bool STREAM>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4))) void nra_kernel(const NraDevArgs a) {
+    constexpr bool PART = ROT == kRotPart;
     constexpr int G = D / 16;        // lanes per head row
     constexpr int RPW = 64 / G;      // head rows per wave
     constexpr int U = kBatch;
     constexpr int D4 = D / 4;        // float4 per cos/sin row
-    // 64-dim heads with whole-head rotary: four lanes hold a 128-byte row,
+    // 64-dim heads in the whole-head layout: four lanes hold a 128-byte row,
     // so one load per lane-vector would read only half of each row's line per
     // instruction (measured ~10 % slower for streaming loads); rows are read
     // in pairs of whole lines instead
@@ -493,11 +497,11 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: cursor math stays scalar
     const int grp = lane / G;        // head-row slot of this lane in the wave
     const int gl = lane % G;         // lane inside the head row
-    const LaneMap lm = lane_map<D, PART>(a.rot, gl);
+    const LaneMap lm = lane_map<D, ROT>(a.rot, gl);
     int ld_o0 = lm.o0, ld_o1 = lm.o1;   // element offsets this lane loads
     if constexpr (PART && D >= 128) {
         if (half_rot) {
-            const LaneMap pm = lane_map<D, PART>(a.rot, G - 1 - gl);
+            const LaneMap pm = lane_map<D, ROT>(a.rot, G - 1 - gl);
             ld_o0 = gl < G / 2 ? lm.o0 : pm.o1;
             ld_o1 = gl < G / 2 ? pm.o0 : lm.o1;
         }
@@ -961,7 +965,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
 }
 
 // workgroups per CU the kernel can keep resident (queried once per device)
-template <int D, int QMODE, bool KVFP8, bool PART, bool STREAM>
+template <int D, int QMODE, bool KVFP8, int ROT, bool STREAM>
 int resident_blocks(size_t lds) {
     static int cached_dev = -1, cached = 0, cached_cus = 0;
     static size_t cached_lds = (size_t)-1;
@@ -969,7 +973,7 @@ int resident_blocks(size_t lds) {
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (dev != cached_dev || lds != cached_lds) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nra_kernel<D, QMODE, KVFP8, PART, STREAM>, kBlockThreads,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nra_kernel<D, QMODE, KVFP8, ROT, STREAM>, kBlockThreads,
                                                          lds) != hipSuccess)
             per_cu = 1;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
@@ -982,13 +986,13 @@ int resident_blocks(size_t lds) {
     return cached;
 }
 
-template <int D, int QMODE, bool KVFP8, bool PART, bool STREAM>
+template <int D, int QMODE, bool KVFP8, int ROT, bool STREAM>
 hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     size_t lds = a.paged ? (size_t)(3 * a.B + 2) * sizeof(int) : 0;
     if (a.stage_q_scale) lds = (size_t)((3 * a.B + 2 + 3) & ~3) * sizeof(int) + (size_t)kMaxTokensPerTile * a.Hq * sizeof(float);
     // enough workgroups to fill every CU, none with less than 8 head-row
     // chunks of work, and at least one per 4 requests for the tail clears
-    const int64_t cap = resident_blocks<D, QMODE, KVFP8, PART, STREAM>(lds);
+    const int64_t cap = resident_blocks<D, QMODE, KVFP8, ROT, STREAM>(lds);
     // 8 (token, chunk) items per workgroup, but 4 for small calls (up to 64
     // workgroups): a tiny decode's time is its latency chain, which more
     // workgroups shorten (16 tokens: 9.4 -> 8.1 us), while at B = 256 the
@@ -1018,7 +1022,7 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     // 15k-token prefill gains about 2 us).  Other layouts keep the plain
     // round-robin, which measured faster for them in steady state.
     la.xcd_spans = (la.interleave > 0 && a.stage_q_scale && la.grid % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, PART, STREAM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
+    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, ROT, STREAM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();
 }
 
@@ -1031,19 +1035,22 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
 #define QKPREP_CAT(x, y) QKPREP_CAT2(x, y)
 
 // Launch for head dim QKPREP_NRA_HEAD_DIM: picks the instance for the Q mode,
-// the cache dtype, whole-head or partial rotary, and streaming or cached
-// qkv loads.  A call without rotated dims takes the whole-head layout, whose
-// load instructions read whole lines.
+// the cache dtype, the rotary layout (whole head, partial, none) and
+// streaming or cached qkv loads.  A call without rotated dims takes the
+// whole-head lane layout, whose load instructions read whole lines.
 hipError_t QKPREP_CAT(launch_norm_rope_append_d, QKPREP_NRA_HEAD_DIM)(const NraDevArgs& a, int q_mode, int kv_fp8,
                                                                        hipStream_t stream) {
     constexpr int D = QKPREP_NRA_HEAD_DIM;
 #define QKPREP_NRA_CASE(QM, KF)                                                                          \
     if (q_mode == QM && (kv_fp8 != 0) == KF) {                                                           \
-        if (a.rot == D || a.rot == 0)                                                                    \
-            return a.stream_qkv ? launch_t<D, QM, KF, false, true>(a, stream)                             \
-                                : launch_t<D, QM, KF, false, false>(a, stream);                           \
-        return a.stream_qkv ? launch_t<D, QM, KF, true, true>(a, stream)                                  \
-                            : launch_t<D, QM, KF, true, false>(a, stream);                                \
+        if (a.rot == D)                                                                                  \
+            return a.stream_qkv ? launch_t<D, QM, KF, kRotWhole, true>(a, stream)                         \
+                                : launch_t<D, QM, KF, kRotWhole, false>(a, stream);                       \
+        if (a.rot == 0)                                                                                  \
+            return a.stream_qkv ? launch_t<D, QM, KF, kRotNone, true>(a, stream)                          \
+                                : launch_t<D, QM, KF, kRotNone, false>(a, stream);                        \
+        return a.stream_qkv ? launch_t<D, QM, KF, kRotPart, true>(a, stream)                              \
+                            : launch_t<D, QM, KF, kRotPart, false>(a, stream);                            \
     }
     QKPREP_NRA_CASE(0, false) QKPREP_NRA_CASE(0, true)
     QKPREP_NRA_CASE(1, false) QKPREP_NRA_CASE(1, true)
