@@ -30,7 +30,7 @@
  *    (reshape_and_cache slot scatter, concat_and_cache_mla latent + rope
  *    concat, interleaved RoPE for DeepSeek MLA; model table).
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *  - cos_sin_cache row p is [cos(p f_0) .. cos(p f_{R/2-1}) | sin(...)].
  *    NeoX pairs (i, i + R/2) use angle i; interleaved pairs (2i, 2i+1) use
  *    angle i.  With R < D the first R dims of a head rotate and the rest

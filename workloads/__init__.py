@@ -9,8 +9,8 @@ torch's conversion (a library routine).
 
 Shapes and distributions follow the five configurations the prepare pass is
 measured on (tiny decode, B=256 decode, ragged FP8 prefill, strided D=256
-Gemma path, MLA concat) -- see ``CONFIGS``.  Input recipes are stated in
-DESIGN.md.
+Gemma path, MLA concat) -- see ``CONFIGS``; each constructor's docstring
+states its recipe.
 """
 from __future__ import annotations
 
