@@ -23,6 +23,7 @@ the same step.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
        python bench.py --suite      (every configuration and variant, one by one)
+       python bench.py --pages-rows (the FlashInfer PR's measured rows, beside its figures)
 """
 from __future__ import annotations
 
@@ -65,7 +66,74 @@ def parse():
     ap.add_argument("--suite-only", default=None, help="comma-separated subset of the suite's workloads")
     ap.add_argument("--suite-launches", type=int, default=200,
                     help="clean-cache launches per session (three sessions) of each suite workload")
+    ap.add_argument("--pages-rows", action="store_true",
+                    help="time the FlashInfer PR's measured rows, rebuilt, after a cache flush each, and "
+                         "print them beside that PR's B200 / H100 latencies (context only)")
     return ap.parse_args()
+
+
+# Latencies in us that the FlashInfer PR (fused QK RMSNorm + NeoX RoPE + FP8
+# E4M3 quantize + NHD paged-KV append) prints for these rows in its
+# Performance section: B200 (sm_100a) and H100 80GB (sm_90a), each the median
+# of a call's kernel activity with a cold L2.  Other hardware: context only.
+PAGES_ROW_US = {
+    "P_decode_64x8_q1_n2": (3.78, 4.22),
+    "P_prefill_64x8_q1_n2": (4.29, 5.22),
+    "P_decode_8x1_q1_n2": (3.26, 3.07),
+    "E_prefill_64x8_q128": (10.75, 11.81),
+    "X_decode_64x8_B1_q1_n2": (3.20, 2.91),
+    "X_decode_64x8_B128_q1_n2": (8.00, 10.46),
+    "X_decode_64x8_B256_q1_n2": (12.19, 18.98),
+    "X_decode_8x1_B256_q1_n2": (4.42, 4.93),
+    "X_prefill_64x8_B1_Q1024_q1_n2": (17.54, 20.22),
+    "X_prefill_8x1_B1_Q1024_q1_n2": (4.45, 5.19),
+}
+
+
+def run_pages_rows(args, dev):
+    """Each of the PR's rows, rebuilt: 20 warm-up launches, then three
+    sessions of --suite-launches launches, each after a clean 512 MiB read
+    flush (HIP events around each launch)."""
+    import torch
+    import workloads as W
+    stream = torch.cuda.current_stream()
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    table = {}
+    for name in W.PAGES_ROWS:
+        log(f"pages row: {name}")
+        inp = W.pages_row(name, host_caches=False)
+        c = Call(inp, dev)
+        for _ in range(20):
+            c.launch()
+        torch.cuda.synchronize()
+        sessions = []
+        for _ in range(3):
+            cold = []
+            for _ in range(args.suite_launches):
+                flush.sum()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                c.launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1) * 1e3)
+            sessions.append(sorted(cold))
+        allc = sorted(x for ses in sessions for x in ses)
+        med = percentile(allc, 0.5)
+        model = c.bytes - inp.algorithmic_bytes()["norm_weights"]
+        b200, h100 = PAGES_ROW_US[name]
+        table[name] = {"tokens": inp.T, "bytes_MB": round(model / 1e6, 3),
+                       "clean_cache_median_us": round(med, 2),
+                       "clean_cache_p10_us": round(percentile(allc, 0.1), 2),
+                       "clean_cache_p90_us": round(percentile(allc, 0.9), 2),
+                       "clean_cache_session_medians_us": [round(percentile(ses, 0.5), 2) for ses in sessions],
+                       "TBps": round(model / med / 1e6, 3),
+                       "pages_B200_us": b200, "pages_H100_us": h100}
+        log(f"  {table[name]}")
+        del c
+        torch.cuda.empty_cache()
+    print(json.dumps({"pages_rows": table, "launches_per_row": 3 * args.suite_launches}), flush=True)
 
 
 def suite_workloads():
@@ -399,6 +467,9 @@ def main():
         return
     if args.suite:
         run_suite(args, dev)
+        return
+    if args.pages_rows:
+        run_pages_rows(args, dev)
         return
 
     log("generating decode B=256")

@@ -991,16 +991,21 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     size_t lds = a.paged ? (size_t)(3 * a.B + 2) * sizeof(int) : 0;
     if (a.stage_q_scale) lds = (size_t)((3 * a.B + 2 + 3) & ~3) * sizeof(int) + (size_t)kMaxTokensPerTile * a.Hq * sizeof(float);
     // enough workgroups to fill every CU, none with less than 8 head-row
-    // chunks of work, and at least one per 4 requests for the tail clears
+    // chunks of work, and at least one per request when tails are cleared
+    // (one per 4 requests otherwise, for the flags)
     const int64_t cap = resident_blocks<D, QMODE, KVFP8, ROT, STREAM>(lds);
     // 8 (token, chunk) items per workgroup, but 4 for small calls (up to 64
     // workgroups): a tiny decode's time is its latency chain, which more
     // workgroups shorten (16 tokens: 9.4 -> 8.1 us), while at B = 256 the
-    // 8-item split measured best
+    // 8-item split measured best.  A decode with few head rows per token and
+    // long tails (8/1 heads, page 64, 256 requests) otherwise gives each
+    // workgroup four requests' tails: one per request took it from 14.8 to
+    // 12.6 us.
     int64_t want = (a.total_items + 7) / 8;
     const int64_t want4 = (a.total_items + 3) / 4;
     if (want < (want4 < 64 ? want4 : 64)) want = want4 < 64 ? want4 : 64;
-    if (want < (a.B + 3) / 4) want = (a.B + 3) / 4;
+    const int64_t per_req = a.zero_tail ? a.B : (a.B + 3) / 4;
+    if (want < per_req) want = per_req;
     if (want < 1) want = 1;
     NraDevArgs la = a;
     la.grid = (int)(want < cap ? want : cap);

@@ -39,7 +39,7 @@ def _tail_rows_by_formula(inp):
     ("c4", 24 * 512 + 1024 + 16 * 512 + 8 * 512 + 4 * 512),
 ])
 def test_norm_rope_append_bytes_per_token(name, per_token):
-    inp = W.CONFIGS[name]()
+    inp = W.CONFIGS[name](**({} if name == "c5" else {"host_caches": False}))
     d = inp.algorithmic_bytes()
     weights = 2 * inp.D * 4
     tails = _tail_rows_by_formula(inp) * 2 * inp.Hkv * inp.D * (1 if inp.kv_fp8 else 2)
@@ -48,16 +48,16 @@ def test_norm_rope_append_bytes_per_token(name, per_token):
 
 
 def test_variant_bytes():
-    c3 = W.c3_prefill_fp8()
+    c3 = W.c3_prefill_fp8(host_caches=False)
     base = c3.algorithmic_bytes()
     # rotary over 64 of 128 dims reads half a cos/sin row; rotary 0 reads none
-    assert W.c3_prefill_fp8(rotary_dim=64).algorithmic_bytes()["total"] == base["total"] - c3.T * 256
-    assert W.c3_prefill_fp8(rotary_dim=0).algorithmic_bytes()["total"] == base["total"] - c3.T * 512
+    assert W.c3_prefill_fp8(rotary_dim=64, host_caches=False).algorithmic_bytes()["total"] == base["total"] - c3.T * 256
+    assert W.c3_prefill_fp8(rotary_dim=0, host_caches=False).algorithmic_bytes()["total"] == base["total"] - c3.T * 512
     # K/V redirect: no tail rows
-    red = W.c3_prefill_fp8(kv_redirect=True).algorithmic_bytes()
+    red = W.c3_prefill_fp8(kv_redirect=True, host_caches=False).algorithmic_bytes()
     assert red["tail_zero"] == 0 and red["total"] == base["total"] - base["tail_zero"]
     # per-token K/V scales: one fp32 per (row, kv head) for K and V, tail rows included
-    tok = W.c3_prefill_fp8(kv_scale_mode=W.KV_SCALE_TOKEN).algorithmic_bytes()
+    tok = W.c3_prefill_fp8(kv_scale_mode=W.KV_SCALE_TOKEN, host_caches=False).algorithmic_bytes()
     tail_rows = _tail_rows_by_formula(c3)
     assert tok["kv_scales"] == (c3.T + tail_rows) * 2 * 8 * 4
     # no tail clear on the decode
@@ -106,3 +106,15 @@ def test_percentile_helper():
     assert bench.percentile(v, 0.1) == pytest.approx(1.9)
     assert bench.percentile([3.0], 0.9) == 3.0
     assert bench.percentile([], 0.5) is None
+
+
+@pytest.mark.parametrize("name", list(W.PAGES_ROWS))
+def test_pages_rows_reproduce_the_printed_bytes(name):
+    """The FlashInfer PR's performance tables print each row's bytes (MB,
+    1e6 B, without the norm weights); the rows rebuilt from their names move
+    exactly that many, so the timings set beside them are for the same
+    traffic."""
+    inp = W.pages_row(name, host_caches=False)
+    d = inp.algorithmic_bytes()
+    assert round((d["total"] - d["norm_weights"]) / 1e6, 3) == W.PAGES_ROWS[name][-1]
+    assert d["norm_weights"] == 2 * 128 * 4

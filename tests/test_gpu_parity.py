@@ -51,6 +51,15 @@ def test_c3_with_an_empty_request():
     print(stats, flush=True)
 
 
+@pytest.mark.parametrize("name", ["X_decode_64x8_B256_q1_n2", "X_decode_8x1_B256_q1_n2", "E_prefill_64x8_q128",
+                                  "P_prefill_64x8_q1_n2", "X_prefill_64x8_B1_Q1024_q1_n2"])
+def test_pages_measured_rows(name):
+    """The FlashInfer PR's measured rows as rebuilt for the benchmark (decode
+    tokens in row 0 of a fresh page, token-major Q scales; prefill requests
+    with padded Q scales and max_seqlen = q_len), on a smaller page pool."""
+    print(run_and_compare(W.pages_row(name, prior_pages=4)), flush=True)
+
+
 def test_c2_full_pool():
     """B=256 decode over the full ~262k-page pool (17 GB of bf16 cache): the
     touched pages are compared with the oracle run on a pool relabelled to

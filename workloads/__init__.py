@@ -484,3 +484,53 @@ CONFIGS = {
     "c4": c4_strided_d256,
     "c5": c5_mla,
 }
+
+
+# ----------------------------------------------------------------------------
+# the rows the FlashInfer PR (fused QK RMSNorm + NeoX RoPE + FP8 E4M3 quantize
+# + NHD paged-KV append) measures in its Performance section
+# ----------------------------------------------------------------------------
+
+# name -> (kind, requests, tokens per request, (Hq, Hkv), Q policy, page size,
+#          printed bytes in MB).  Every row has D = 128, bf16 qkv, E4M3 Q and
+# E4M3 caches, norm policy 2; Q policy 1 is the dynamic per-token-head scale.
+PAGES_ROWS = {
+    "P_decode_64x8_q1_n2": ("decode", 32, 1, (64, 8), 1, 64, 5.136),
+    "P_prefill_64x8_q1_n2": ("prefill", 8, 16, (64, 8), 1, 64, 4.817),
+    "P_decode_8x1_q1_n2": ("decode", 32, 1, (8, 1), 1, 64, 0.656),
+    "E_prefill_64x8_q128": ("prefill", 4, 128, (64, 8), 1, 64, 16.122),
+    "X_decode_64x8_B1_q1_n2": ("decode", 1, 1, (64, 8), 1, 64, 0.161),
+    "X_decode_64x8_B128_q1_n2": ("decode", 128, 1, (64, 8), 1, 64, 20.546),
+    "X_decode_64x8_B256_q1_n2": ("decode", 256, 1, (64, 8), 1, 64, 41.091),
+    "X_decode_8x1_B256_q1_n2": ("decode", 256, 1, (8, 1), 1, 64, 5.251),
+    "X_prefill_64x8_B1_Q1024_q1_n2": ("prefill", 1, 1024, (64, 8), 1, 64, 32.244),
+    "X_prefill_8x1_B1_Q1024_q1_n2": ("prefill", 1, 1024, (8, 1), 1, 64, 4.489),
+}
+
+
+def pages_row(name, seed=2001, prior_pages=64, **kw):
+    """One of the FlashInfer PR's measured rows, rebuilt from its name.
+
+    Decode rows: each request appends one token after a prior length that is
+    a multiple of the page size (U[0, prior_pages) pages), so the token lands in row 0
+    of a fresh page and the rest of that page is tail; Q scales token-major
+    [T, Hq].  Prefill rows: fresh requests (prior 0) of equal length, Q
+    scales in the padded [B, Hq, round_up(q_len, 128)] layout with
+    max_seqlen = q_len.  qkv ~ N(0, 1); norm policy 2 read as the (1 + w)
+    weighting; k_scale = v_scale = 0.05; upper_max 448; theta 1e6, table
+    [8192, 128].  The byte model of these rows (qkv read, E4M3 Q and its
+    scales, cos/sin rows, K/V append, tail rows; no norm weights) then gives
+    the printed megabytes."""
+    kind, B, q, (hq, hkv), qpol, ps, _ = PAGES_ROWS[name]
+    rng = np.random.default_rng(seed)
+    if kind == "decode":
+        prior = ps * rng.integers(0, prior_pages, size=B)
+    else:
+        prior = np.zeros(B, np.int64)
+    args = dict(name=name, seed=seed + 7, q_lens=np.full(B, q, np.int64), prior_lens=prior,
+                Hq=hq, Hkv=hkv, D=128, page_size=ps, norm=NORM_GEMMA, theta=1e6, cs_rows=8192,
+                kv_fp8=True, q_mode=Q_FP8_DYNAMIC if qpol == 1 else Q_FP8_STATIC,
+                q_scale_padded=kind == "prefill", max_seqlen=q if kind == "prefill" else 0,
+                upper_max=448.0, q_scale_inv=2.0, k_scale=0.05, v_scale=0.05)
+    args.update(kw)
+    return nra_case(**args)
