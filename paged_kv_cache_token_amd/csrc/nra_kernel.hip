@@ -104,8 +104,11 @@ __device__ __forceinline__ ReqPages request_pages(const NraDevArgs& a, const int
 constexpr int kPageSlots = kBlockThreads;   // pages located by table lookup (one per thread)
 constexpr int kSearchRequests = 64;         // up to this many requests, pages are found by binary search
 
+// The same pass also writes the request of each of the first tile's tokens
+// (s_treq[t - t_first] for t in [t_first, t_first + ntok)), since it visits
+// each request's q_indptr range anyway.
 __device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen, int* s_pre,
-                                 int* s_wave, int* s_pgreq, int* s_pgcol) {
+                                 int* s_wave, int* s_pgreq, int* s_pgcol, int* s_treq, int t_first, int ntok) {
     const int tid = threadIdx.x;
     const int B = a.B;
     int bad = 0;
@@ -113,8 +116,12 @@ __device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const
     const int per = (B + kBlockThreads - 1) / kBlockThreads;
     const int lo = min(B, tid * per), hi = min(B, lo + per);
     int sum = 0;
+    ReqPages rp_lo{0, 0, 0};   // request lo's pages, kept for the second pass
     for (int b = lo; b < hi; ++b) {
+        const int t0 = max(s_indptr[b], t_first), t1 = min(s_indptr[b + 1], t_first + ntok);
+        for (int t = t0; t < t1; ++t) s_treq[t - t_first] = b;
         ReqPages rp = request_pages(a, s_indptr, s_seqlen, b);
+        if (b == lo) rp_lo = rp;
         bad |= rp.bad;
         sum += rp.count;
     }
@@ -127,7 +134,7 @@ __device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const
     int run = base + incl - sum;
     for (int b = lo; b < hi; ++b) {
         s_pre[b] = run;
-        const ReqPages rp = request_pages(a, s_indptr, s_seqlen, b);
+        const ReqPages rp = b == lo ? rp_lo : request_pages(a, s_indptr, s_seqlen, b);
         // the first kPageSlots pages of the call: their request and column
         // (many requests: each writes its few slots; few requests find their
         // pages by binary search instead, see page_slot_ptr)
@@ -818,8 +825,10 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     kc.q_static = q_static_v;
     int bad = 0;
     if (a.paged) {
-        scatter_tokens();   // made visible by the barriers inside the validation
-        bad = validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave, s_pgreq, s_pgcol);
+        // (the first tile's token -> request map is written in the same
+        // pass; the barriers inside make it visible)
+        bad = validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave, s_pgreq, s_pgcol, s_treq, t_first,
+                                have_items ? ntok : 0);
     }
     {
         // The page-id checks, the tile's row lookups and cos/sin loads and the
