@@ -107,15 +107,31 @@ constexpr int kSearchRequests = 64;         // up to this many requests, pages a
 // The same pass also writes the request of each of the first tile's tokens
 // (s_treq[t - t_first] for t in [t_first, t_first + ntok)), since it visits
 // each request's q_indptr range anyway.
-__device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen, int* s_pre,
-                                 int* s_wave, int* s_pgreq, int* s_pgcol, int* s_treq, int t_first, int ntok) {
+//
+// Short path: with at most one request per thread and at most kFastPages
+// pages per request (decodes, short prefills), each thread reads its own
+// request's page ids right away, and the prefix and page slots are skipped
+// (one barrier fewer; the page reads overlap the row lookups).  The choice
+// is the same in every thread: a vote published by the pass's barrier.
+constexpr int kFastPages = 2;
+
+struct Verdict {
+    int bad;        // this thread's partial verdict (page-id checks of the short path not yet applied)
+    int fast;       // short path taken (uniform over the workgroup)
+    int pg0, pg1;   // short path: the page ids of this thread's request
+    int npg;        // short path: how many of pg0 / pg1 to check
+};
+
+__device__ Verdict validate_requests(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen, int* s_pre,
+                                     int* s_wave, int* s_vote, int* s_pgreq, int* s_pgcol, int* s_treq,
+                                     int t_first, int ntok) {
     const int tid = threadIdx.x;
     const int B = a.B;
     int bad = 0;
     if (tid == 0 && (s_indptr[0] != 0 || s_indptr[B] != a.T)) bad = 1;
     const int per = (B + kBlockThreads - 1) / kBlockThreads;
     const int lo = min(B, tid * per), hi = min(B, lo + per);
-    int sum = 0;
+    int sum = 0, few = 1;
     ReqPages rp_lo{0, 0, 0};   // request lo's pages, kept for the second pass
     for (int b = lo; b < hi; ++b) {
         const int t0 = max(s_indptr[b], t_first), t1 = min(s_indptr[b + 1], t_first + ntok);
@@ -124,11 +140,23 @@ __device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const
         if (b == lo) rp_lo = rp;
         bad |= rp.bad;
         sum += rp.count;
+        few &= rp.count <= kFastPages ? 1 : 0;
     }
+    // the own request's page ids (a valid request's pages lie inside its
+    // page-table row; an invalid one has count 0 and reads the zero row)
+    const int own = (per == 1 && lo < hi) ? rp_lo.count : 0;
+    const int* zi = reinterpret_cast<const int*>(g_zero_row);
+    const int* q0 = own >= 1 ? a.page_table + (int64_t)lo * a.maxp + rp_lo.first : zi;
+    const int pg0 = gld(q0);
+    const int pg1 = gld(own >= 2 ? q0 + 1 : zi);
     const int lane = tid & 63, wave = tid >> 6;
     const int incl = wave_inclusive_scan(sum);
     if (lane == 63) s_wave[wave] = incl;
+    const bool wave_few = __ballot(few == 0) == 0;
+    if (lane == 0) s_vote[wave] = wave_few ? 1 : 0;
     __syncthreads();
+    if (per == 1 && (s_vote[0] & s_vote[1] & s_vote[2] & s_vote[3]))
+        return Verdict{bad, 1, pg0, pg1, own};
     int base = 0;
     for (int w = 0; w < wave; ++w) base += s_wave[w];
     int run = base + incl - sum;
@@ -146,7 +174,7 @@ __device__ int validate_requests(const NraDevArgs& a, const int* s_indptr, const
     }
     if (tid == kBlockThreads - 1) s_pre[B] = base + incl;
     __syncthreads();
-    return bad;
+    return Verdict{bad, 0, 0, 0, 0};
 }
 
 // Validation, step 2: every page id the call writes must lie in the pool.
@@ -485,6 +513,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     // q_indptr [B+1] | seq_lens [B] | page prefix [B+1] | (padded q_scale) staged scales [TPB][Hq]
     extern __shared__ int s_dyn[];
     __shared__ int s_wave[4];
+    __shared__ int s_vote[4];
     __shared__ __align__(16) float s_w[2 * D];                       // q | k norm weights
     __shared__ __align__(16) float s_cs[kMaxTokensPerTile * D];      // cos/sin rows of the tile
     __shared__ int s_pos[kMaxTokensPerTile];
@@ -824,11 +853,13 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     kc.inv_v = 1.0f / v_scale_v;
     kc.q_static = q_static_v;
     int bad = 0;
+    Verdict vd{0, 0, 0, 0, 0};
     if (a.paged) {
         // (the first tile's token -> request map is written in the same
         // pass; the barriers inside make it visible)
-        bad = validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave, s_pgreq, s_pgcol, s_treq, t_first,
-                                have_items ? ntok : 0);
+        vd = validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave, s_vote, s_pgreq, s_pgcol, s_treq, t_first,
+                               have_items ? ntok : 0);
+        bad = vd.bad;
     }
     {
         // The page-id checks, the tile's row lookups and cos/sin loads and the
@@ -836,7 +867,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
         // reads stay inside the page table even for malformed metadata (the
         // page counts of an inconsistent request are zero and the row lookups
         // are clamped); nothing is written unless the whole call is valid.
-        const int total_pages = a.paged ? s_pre[a.B] : 0;
+        const int total_pages = (a.paged && !vd.fast) ? s_pre[a.B] : 0;
         const int ks = min(tid, max(min(total_pages, kPageSlots) - 1, 0));
         const int* pp = reinterpret_cast<const int*>(g_zero_row);
         if (total_pages > 0)
@@ -847,6 +878,8 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
         const int tail_page = fetch_tail();
         if (have_items) store_rows(rf);
         if (a.paged) store_tail(tail_page);
+        if (vd.npg >= 1) bad |= page_out_of_pool(a, vd.pg0);
+        if (vd.npg >= 2) bad |= page_out_of_pool(a, vd.pg1);
         if (tid < total_pages) bad |= page_out_of_pool(a, p_first);
         for (int k = tid + kBlockThreads; k < total_pages; k += kBlockThreads)
             bad |= page_out_of_pool(a, page_id_at(a, s_indptr, s_seqlen, s_pre, k));
