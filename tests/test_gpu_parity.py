@@ -418,6 +418,45 @@ def test_out_of_pool_page_in_each_check_path(b, which):
     assert (H.oracle_outputs(inp)["flags"] == -1).all()
 
 
+@pytest.mark.parametrize("b,which,long_req", [(0, 0, None), (70, 1, None), (255, 1, None), (130, 0, 131),
+                                               (200, 1, 3)])
+def test_out_of_pool_page_short_validation_path(b, which, long_req):
+    """256 requests writing two pages each (2 tokens across a page boundary)
+    take the short validation path, where each thread checks its own
+    request's page ids; one request writing three or more pages sends the
+    call down the full path.  A page id past the pool as a request's 1st or
+    2nd written page rejects the whole call in both."""
+    B = 256
+    q = np.full(B, 2, dtype=np.int64)
+    prior = 4 * (np.arange(B, dtype=np.int64) % 5) + 3
+    if long_req is not None:
+        q[long_req] = 9
+    inp = W.nra_case(seed=700 + b + which, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=4, maxp=8)
+    first = int(prior[b]) // 4
+    inp.page_table[b, first + which] = inp.num_pages + 1
+    dev = H.DeviceNra(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    gpu = dev.host_outputs()
+    assert (gpu["flags"] == -1).all()
+    H.check_exact(gpu["k_cache"], inp.k_cache0, "k_cache")
+    H.check_exact(gpu["v_cache"], inp.v_cache0, "v_cache")
+    assert (H.oracle_outputs(inp)["flags"] == -1).all()
+
+
+@pytest.mark.parametrize("long_req", [None, 0, 255])
+def test_short_and_full_validation_paths_agree_on_valid_calls(long_req):
+    """The same 256 two-page requests, valid, with and without one request
+    long enough to force the full validation path: outputs match the oracle."""
+    B = 256
+    q = np.full(B, 2, dtype=np.int64)
+    prior = 4 * (np.arange(B, dtype=np.int64) % 5) + 3
+    if long_req is not None:
+        q[long_req] = 9
+    run_and_compare(W.nra_case(seed=710, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=4, maxp=8))
+
+
 def test_many_requests_cross_page_ragged():
     rng = np.random.default_rng(99)
     B = 300
