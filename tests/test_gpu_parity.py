@@ -457,6 +457,34 @@ def test_short_and_full_validation_paths_agree_on_valid_calls(long_req):
     run_and_compare(W.nra_case(seed=710, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=4, maxp=8))
 
 
+@pytest.mark.parametrize("bad_tail", [False, True])
+def test_short_validation_path_with_empty_requests(bad_tail):
+    """A decode batch (short validation path) where some requests append
+    nothing: an empty request with cached rows still has its last page's
+    tail cleared, so that page is checked too; one past the pool rejects
+    the call.  Requests with no rows at all touch no page."""
+    B = 40
+    q = np.ones(B, dtype=np.int64)
+    q[[3, 17, 30]] = 0
+    prior = (np.arange(B, dtype=np.int64) * 7) % 50
+    prior[30] = 0                      # empty and no cached rows
+    inp = W.nra_case(seed=720 + bad_tail, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=16, maxp=8)
+    if not bad_tail:
+        run_and_compare(inp)
+        return
+    sl = int(prior[17])
+    inp.page_table[17, (sl - 1) // 16] = inp.num_pages + 3
+    dev = H.DeviceNra(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    gpu = dev.host_outputs()
+    assert (gpu["flags"] == -1).all()
+    H.check_exact(gpu["k_cache"], inp.k_cache0, "k_cache")
+    H.check_exact(gpu["v_cache"], inp.v_cache0, "v_cache")
+    assert (H.oracle_outputs(inp)["flags"] == -1).all()
+
+
 def test_many_requests_cross_page_ragged():
     rng = np.random.default_rng(99)
     B = 300
