@@ -201,7 +201,8 @@ typedef struct qkprep_norm_rope_append_params {
      * [num_pages * page_size][Hkv][D / g] indexed by the cache row
      * page * page_size + row (or [T][Hkv][D / g] by token with out_k / out_v).
      * A cleared tail row gets zero scales.  Needs the FP8 cache; GROUP needs
-     * kv_group_size a power of two in [8, D/2] (or D) and rotary_dim == D. */
+     * kv_group_size a power of two in [8, D/2] (or D), and a group smaller
+     * than the head needs rotary_dim == D or 0. */
     int32_t kv_scale_mode;         /* qkprep_kv_scale_mode */
     int32_t kv_group_size;
     float* k_scale_out;

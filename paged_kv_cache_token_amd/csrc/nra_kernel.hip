@@ -15,7 +15,8 @@
 //    (R rotated dims), else the 16 pass-through elements [16l, 16l+16).
 //    Every NeoX pair (i, i + R/2) and every interleaved pair (2i, 2i+1) then
 //    sits in one lane's registers: RoPE needs no lane exchange.  The common
-//    R = D case is a separate instance with compile-time offsets.  A wave
+//    R = D case is a separate instance with compile-time offsets, and R = 0
+//    (no rotated dims) runs that layout with RoPE compiled out.  A wave
 //    covers 64/G head rows of one token (a "chunk").
 //  * The sum of squares and the FP8 amax are reduced over the G lanes of the
 //    row only (DPP within the lane group), never across rows or tokens.
@@ -30,15 +31,16 @@
 //  * Loads are double-buffered and unconditional (rows past the run are
 //    clamped to a valid row) so that the wait for one batch never drains the
 //    loads of the next one.  Where one row's 128-byte line is split between
-//    lanes (64-dim heads, rotary over half the head), rows are loaded one
-//    whole line per instruction and completed by a DPP mirror exchange.
+//    lanes (64-dim heads, rotary over at most half the head), rows are loaded
+//    one whole line per instruction and completed by a DPP mirror exchange.
 //  * All-or-nothing validation without a host sync or a second kernel:
 //    every workgroup stages q_indptr / seq_lens in LDS, checks every request
-//    and every page id the call will write (the pages are enumerated through
-//    a wave prefix sum so each thread checks about one page), and reduces the
-//    verdict with one barrier.  Every workgroup reads the same metadata, so
-//    all reach the same verdict.  An invalid call makes the workgroups write
-//    -1 flags and nothing else.
+//    and every page id the call will write, and reduces the verdict with one
+//    barrier.  When every request writes at most two pages, each thread
+//    checks its own request's pages; otherwise the pages are enumerated
+//    through a prefix sum so that each thread checks about one.  Every
+//    workgroup reads the same metadata, so all reach the same verdict.  An
+//    invalid call makes the workgroups write -1 flags and nothing else.
 //  * The latency chain of a small call is kept at two dependent memory
 //    rounds: the first batch of qkv loads leaves at kernel entry, and the
 //    page checks, row lookups, cos/sin rows and tail pages all issue in the
@@ -96,11 +98,11 @@ __device__ __forceinline__ ReqPages request_pages(const NraDevArgs& a, const int
     return r;
 }
 
-// Validation, step 1 (LDS only): per-request checks and the block-wide
-// exclusive prefix s_pre[0..B] of the number of pages each request writes,
-// with the request and page-table column of each of the first kPageSlots
-// pages (s_pgreq / s_pgcol).  Needs s_indptr / s_seqlen staged.  Returns
-// this thread's partial verdict.
+// Validation, step 1: per-request checks and, on the full path, the
+// block-wide exclusive prefix s_pre[0..B] of the number of pages each
+// request writes, with the request and page-table column of each of the
+// first kPageSlots pages (s_pgreq / s_pgcol).  Needs s_indptr / s_seqlen
+// staged.  Returns this thread's partial verdict and the path taken.
 constexpr int kPageSlots = kBlockThreads;   // pages located by table lookup (one per thread)
 constexpr int kSearchRequests = 64;         // up to this many requests, pages are found by binary search
 
@@ -165,7 +167,7 @@ __device__ Verdict validate_requests(const NraDevArgs& a, const int* s_indptr, c
         const ReqPages rp = b == lo ? rp_lo : request_pages(a, s_indptr, s_seqlen, b);
         // the first kPageSlots pages of the call: their request and column
         // (many requests: each writes its few slots; few requests find their
-        // pages by binary search instead, see page_slot_ptr)
+        // pages by binary search instead, see page_id_ptr)
         for (int k = run; a.B > kSearchRequests && k < min(run + rp.count, kPageSlots); ++k) {
             s_pgreq[k] = b;
             s_pgcol[k] = rp.first + (k - run);
