@@ -31,8 +31,9 @@
 //  * Loads are double-buffered and unconditional (rows past the run are
 //    clamped to a valid row) so that the wait for one batch never drains the
 //    loads of the next one.  Where one row's 128-byte line is split between
-//    lanes (64-dim heads, rotary over at most half the head), rows are loaded
-//    one whole line per instruction and completed by a DPP mirror exchange.
+//    lanes (64-dim heads, partial rotary with 8 or 16 lanes per row), rows are
+//    loaded one whole line per instruction and completed by a DPP mirror
+//    exchange.
 //  * All-or-nothing validation without a host sync or a second kernel:
 //    every workgroup stages q_indptr / seq_lens in LDS, checks every request
 //    and every page id the call will write, and reduces the verdict with one
@@ -510,6 +511,12 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     // vector and its mirror partner's (or the partner's and its own
     // second-half one), and a mirror exchange hands every lane its own
     const bool half_rot = PART && D >= 128 && 2 * a.rot <= D;
+    // Rotary over more than half the head: with P = G - R/16 pass-through
+    // lanes, the P lowest lanes (rope lanes) and the P highest (pass lanes)
+    // hold the two lines' leftover vectors of each other, so they load for
+    // their mirror partner and trade; the rope lanes in between load their
+    // own two vectors
+    const bool wide_rot = PART && D >= 128 && 2 * a.rot > D;
     typedef typename KvType<D, QMODE, KVFP8>::type kv_t;
 
     // q_indptr [B+1] | seq_lens [B] | page prefix [B+1] | (padded q_scale) staged scales [TPB][Hq]
@@ -537,11 +544,18 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     const int gl = lane % G;         // lane inside the head row
     const LaneMap lm = lane_map<D, ROT>(a.rot, gl);
     int ld_o0 = lm.o0, ld_o1 = lm.o1;   // element offsets this lane loads
+    bool xlo = false, xhi = false;       // lane trades its second / first vector
     if constexpr (PART && D >= 128) {
-        if (half_rot) {
-            const LaneMap pm = lane_map<D, ROT>(a.rot, G - 1 - gl);
-            ld_o0 = gl < G / 2 ? lm.o0 : pm.o1;
-            ld_o1 = gl < G / 2 ? pm.o0 : lm.o1;
+        const LaneMap pm = lane_map<D, ROT>(a.rot, G - 1 - gl);
+        const int P = half_rot ? G / 2 : G - (a.rot >> 4);
+        xlo = gl < P;
+        xhi = gl >= G - P;
+        if (xlo) {
+            ld_o0 = lm.o0;
+            ld_o1 = pm.o0;
+        } else if (xhi) {
+            ld_o0 = pm.o1;
+            ld_o1 = lm.o1;
         }
     }
     int* s_indptr = s_dyn;
@@ -897,9 +911,11 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
                 if constexpr (kPairRows) mirror_exchange<kDppRowHalfMirror, 0xA, 0x5>(buf[u][0], buf[u][1]);
                 if constexpr (PART && D == 128) {
                     if (half_rot) mirror_exchange<kDppRowHalfMirror, 0xA, 0x5>(buf[u][0], buf[u][1]);
+                    else if (wide_rot) mirror_exchange_sel<kDppRowHalfMirror>(buf[u][0], buf[u][1], xhi, xlo);
                 }
                 if constexpr (PART && D == 256) {
                     if (half_rot) mirror_exchange<kDppRowMirror, 0xC, 0x3>(buf[u][0], buf[u][1]);
+                    else if (wide_rot) mirror_exchange_sel<kDppRowMirror>(buf[u][0], buf[u][1], xhi, xlo);
                 }
                 const int r = pr.c * RPW + grp;
                 const int ti = pr.t - t_first;

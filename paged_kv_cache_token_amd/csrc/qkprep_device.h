@@ -267,6 +267,27 @@ __device__ __forceinline__ void mirror_exchange(uint4& v0, uint4& v1) {
     v1 = g;
 }
 
+// The same exchange for rotary over more than half the head: with P
+// pass-through lanes per row, only the P lowest lanes (rope lanes that loaded
+// their mirror partner's first vector as v1) and the P highest (pass lanes
+// that loaded their partner's second vector as v0) trade; the rope lanes in
+// between loaded both of their own vectors.  Every lane takes the mirrored
+// value and keeps it only where it receives.
+template <int CTRL>
+__device__ __forceinline__ void mirror_exchange_sel(uint4& v0, uint4& v1, bool recv_first, bool recv_second) {
+    uint4 f, g;
+    f.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.x, (int)v1.x, CTRL, 0xF, 0xF, false);
+    f.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.y, (int)v1.y, CTRL, 0xF, 0xF, false);
+    f.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.z, (int)v1.z, CTRL, 0xF, 0xF, false);
+    f.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v0.w, (int)v1.w, CTRL, 0xF, 0xF, false);
+    g.x = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.x, (int)v0.x, CTRL, 0xF, 0xF, false);
+    g.y = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.y, (int)v0.y, CTRL, 0xF, 0xF, false);
+    g.z = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.z, (int)v0.z, CTRL, 0xF, 0xF, false);
+    g.w = (uint32_t)__builtin_amdgcn_update_dpp((int)v1.w, (int)v0.w, CTRL, 0xF, 0xF, false);
+    if (recv_first) v0 = f;
+    if (recv_second) v1 = g;
+}
+
 // ---------------------------------------------------------------------------
 // wave and block primitives
 // ---------------------------------------------------------------------------

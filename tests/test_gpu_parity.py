@@ -135,8 +135,9 @@ def test_heads_pages_rope(rope, heads, ps):
 # R/2 a multiple of 16 pairs the rope lanes for 16-byte FP8 stores, other R
 # store 8-byte halves; R = 0 reads no positions
 @pytest.mark.parametrize("D,R", [(128, 64), (128, 32), (128, 96), (128, 48), (128, 16), (128, 0),
+                                 (128, 80), (128, 112),
                                  (256, 128), (256, 80), (256, 64), (256, 112), (256, 16),
-                                 (256, 160), (64, 32), (64, 16), (64, 48), (64, 0)])
+                                 (256, 160), (256, 144), (256, 240), (64, 32), (64, 16), (64, 48), (64, 0)])
 @pytest.mark.parametrize("arm", ["fp8", "bf16"])
 def test_partial_rotary(D, R, arm):
     q, prior = _ragged(D + R, B=5, max_q=30, max_prior=200)
@@ -169,10 +170,11 @@ def test_nope_layer_full_size_prefill():
     print(run_and_compare(W.c3_prefill_fp8(rotary_dim=0)), flush=True)
 
 
-@pytest.mark.parametrize("D,R", [(128, 64), (128, 32), (256, 64)])
+@pytest.mark.parametrize("D,R", [(128, 64), (128, 32), (256, 64), (128, 96), (256, 192)])
 def test_partial_rotary_full_size_prefill(D, R):
-    """The 15k-token FP8 prefill with rotary over at most half the head:
-    round-robin spans, and the mirrored loads that read whole lines."""
+    """The 15k-token FP8 prefill with partial rotary: round-robin spans, and
+    the mirrored loads that read whole lines (all lanes trade up to half the
+    head; beyond it only the outer lanes of each row do)."""
     print(run_and_compare(W.c3_prefill_fp8(D=D, rotary_dim=R)), flush=True)
 
 
