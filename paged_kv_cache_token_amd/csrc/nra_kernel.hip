@@ -499,11 +499,11 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     constexpr int RPW = 64 / G;      // head rows per wave
     constexpr int U = kBatch;
     constexpr int D4 = D / 4;        // float4 per cos/sin row
-    // 64-dim heads in the whole-head layout: four lanes hold a 128-byte row,
-    // so one load per lane-vector would read only half of each row's line per
-    // instruction (measured ~10 % slower for streaming loads); rows are read
-    // in pairs of whole lines instead
-    constexpr bool kPairRows = D == 64 && !PART;
+    // 64-dim heads: four lanes hold a 128-byte row, so one load per
+    // lane-vector would read only half of each row's line per instruction
+    // (measured ~10 % slower for streaming loads); rows are read in pairs of
+    // whole lines instead, in every rotary layout
+    constexpr bool kPairRows = D == 64;
     // Rotary over at most half the head (8 or 16 lanes per row): lanes
     // 0 .. G/2-1 then hold exactly the first half of the row, but the rope
     // lanes' two vectors lie R/2 apart, so one load instruction would touch
@@ -544,6 +544,16 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     const int gl = lane % G;         // lane inside the head row
     const LaneMap lm = lane_map<D, ROT>(a.rot, gl);
     int ld_o0 = lm.o0, ld_o1 = lm.o1;   // element offsets this lane loads
+    if constexpr (kPairRows) {
+        // rows 2p and 2p+1: a lane of row 2p loads its own first vector and
+        // the first vector of its mirror partner in row 2p+1 (lane G-1-gl
+        // there); a lane of row 2p+1 loads its partner's second vector in
+        // row 2p and its own second vector
+        const LaneMap pm = lane_map<D, ROT>(a.rot, G - 1 - gl);
+        const bool even = (grp & 1) == 0;
+        ld_o0 = even ? lm.o0 : pm.o1;
+        ld_o1 = even ? pm.o0 : lm.o1;
+    }
     bool xlo = false, xhi = false;       // lane trades its second / first vector
     if constexpr (PART && D >= 128) {
         const LaneMap pm = lane_map<D, ROT>(a.rot, G - 1 - gl);
@@ -618,9 +628,8 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
                 // lanes its second vectors, mirrored), the second the whole
                 // line of row 2p+1; pair_exchange then gives every lane its own
                 const int ra = ld.c * RPW + (grp & ~1), rb = ra + 1;
-                const bool even = (grp & 1) == 0;
-                const uint16_t* sa = tok + ((ld.left > 0 && ra < a.R) ? ra : 0) * D + (even ? 8 * gl : 56 - 8 * gl);
-                const uint16_t* sb = tok + ((ld.left > 0 && rb < a.R) ? rb : 0) * D + (even ? 24 - 8 * gl : 32 + 8 * gl);
+                const uint16_t* sa = tok + ((ld.left > 0 && ra < a.R) ? ra : 0) * D + ld_o0;
+                const uint16_t* sb = tok + ((ld.left > 0 && rb < a.R) ? rb : 0) * D + ld_o1;
                 if constexpr (STREAM) {
                     buf[u][0] = ld16_stream(sa);
                     buf[u][1] = ld16_stream(sb);

@@ -242,11 +242,14 @@ __device__ __forceinline__ float max_nonneg(float a, float b) {
 // and lanes in the banks of RECV_FIRST take the partner's v1 as their first
 // vector, lanes in the banks of RECV_SECOND the partner's v0 as their second
 // (DPP banks are the 4-lane groups of each 16-lane row).
-//  - Four lanes per 128-byte row (row_half_mirror, 0xA / 0x5), elements
-//    [8 gl, +8) and [32 + 8 gl, +8) of the row per lane: lanes 8p .. 8p+3 (row 2p,
-//    lane gl) loaded v0 = row 2p [8 gl, +8) and v1 = row 2p+1 [24 - 8 gl, +8);
-//    lanes 8p+4+k (row 2p+1) loaded v0 = row 2p [56 - 8k, +8) and v1 = row
-//    2p+1 [32 + 8k, +8).
+//  - Four lanes per 128-byte row (row_half_mirror, 0xA / 0x5): lanes
+//    8p .. 8p+3 (row 2p) loaded v0 = their own first vector and v1 = the
+//    first vector of their mirror partner in row 2p+1; lanes 8p+4 .. 8p+7
+//    (row 2p+1) loaded v0 = their partner's second vector in row 2p and v1 =
+//    their own second vector.  In the whole-head layout (elements [8 gl, +8)
+//    and [32 + 8 gl, +8) per lane) that is row 2p [8 gl, +8) and row 2p+1
+//    [24 - 8 gl, +8) for lane gl of row 2p, row 2p [56 - 8k, +8) and row 2p+1
+//    [32 + 8k, +8) for lane k of row 2p+1.
 //  - Rotary over half the head, 8 or 16 lanes per row (row_half_mirror 0xA /
 //    0x5, or row_mirror 0xC / 0x3): rope lane gl (< G/2) loaded v0 = [8 gl,
 //    +8) and v1 = the first vector [16 (G-1-gl), +8) of pass lane G-1-gl; pass

@@ -170,7 +170,7 @@ def test_nope_layer_full_size_prefill():
     print(run_and_compare(W.c3_prefill_fp8(rotary_dim=0)), flush=True)
 
 
-@pytest.mark.parametrize("D,R", [(128, 64), (128, 32), (256, 64), (128, 96), (256, 192)])
+@pytest.mark.parametrize("D,R", [(128, 64), (128, 32), (256, 64), (128, 96), (256, 192), (64, 32)])
 def test_partial_rotary_full_size_prefill(D, R):
     """The 15k-token FP8 prefill with partial rotary: round-robin spans, and
     the mirrored loads that read whole lines (all lanes trade up to half the
