@@ -152,6 +152,8 @@ def suite_workloads():
         "prefill_d64_gqa_64_8": (lambda: W.c3_prefill_fp8(D=64, name="prefill_d64"), "nra"),
         "prefill_rotary_64_of_128": (lambda: W.c3_prefill_fp8(rotary_dim=64, name="prefill_r64"), "nra"),
         "prefill_nope_layer": (lambda: W.c3_prefill_fp8(rotary_dim=0, name="prefill_r0"), "nra"),
+        "prefill_rotary_96_of_128": (lambda: W.c3_prefill_fp8(rotary_dim=96, name="prefill_r96"), "nra"),
+        "prefill_d64_rotary_32_of_64": (lambda: W.c3_prefill_fp8(D=64, rotary_dim=32, name="prefill_d64_r32"), "nra"),
         "c5_mla_q_fp8_dynamic": (lambda: W.c5_mla(q_mode=W.Q_FP8_DYNAMIC), "mla"),
         "c5_mla_q_fp8_static": (lambda: W.c5_mla(q_mode=W.Q_FP8_STATIC), "mla"),
         "prefill_kv_token_scales": (lambda: W.c3_prefill_fp8(kv_scale_mode=W.KV_SCALE_TOKEN), "nra"),

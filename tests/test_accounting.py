@@ -53,6 +53,7 @@ def test_variant_bytes():
     # rotary over 64 of 128 dims reads half a cos/sin row; rotary 0 reads none
     assert W.c3_prefill_fp8(rotary_dim=64, host_caches=False).algorithmic_bytes()["total"] == base["total"] - c3.T * 256
     assert W.c3_prefill_fp8(rotary_dim=0, host_caches=False).algorithmic_bytes()["total"] == base["total"] - c3.T * 512
+    assert W.c3_prefill_fp8(rotary_dim=96, host_caches=False).algorithmic_bytes()["total"] == base["total"] - c3.T * 128
     # K/V redirect: no tail rows
     red = W.c3_prefill_fp8(kv_redirect=True, host_caches=False).algorithmic_bytes()
     assert red["tail_zero"] == 0 and red["total"] == base["total"] - base["tail_zero"]
