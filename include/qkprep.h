@@ -127,7 +127,7 @@ typedef enum {
 typedef struct qkprep_norm_rope_append_params {
     uint32_t struct_size;          /* = sizeof(qkprep_norm_rope_append_params) */
 
-    int32_t num_tokens;            /* T >= 0 */
+    int32_t num_tokens;            /* T >= 0; T * ceil((Hq + 2 Hkv) / (64 / (D / 16))) < 2^31 */
     int32_t num_q_heads;           /* Hq >= 1 */
     int32_t num_kv_heads;          /* Hkv >= 1, Hq % Hkv == 0 */
     int32_t head_dim;              /* D: 64, 128 or 256 */
@@ -228,7 +228,7 @@ typedef struct qkprep_norm_rope_append_params {
 typedef struct qkprep_mla_params {
     uint32_t struct_size;          /* = sizeof(qkprep_mla_params) */
 
-    int32_t num_tokens;            /* T >= 0 */
+    int32_t num_tokens;            /* T >= 0; T * (ceil(H / 16) + 1) < 2^31 */
     int32_t num_q_heads;           /* H >= 1 */
     int32_t nope_dim;              /* >= 0, multiple of 8 */
     int32_t rope_dim;              /* 64 */

@@ -175,6 +175,8 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     a.chunks_per_token = (R + rows_per_wave - 1) / rows_per_wave;
     a.tokens_per_tile = kMaxTokensPerTile;
     a.total_items = (int64_t)T * a.chunks_per_token;
+    // the kernel indexes (token, chunk) items with 32-bit integers
+    if (a.total_items > INT32_MAX) return QKPREP_E_SHAPE;
 
     hipError_t e = launch_norm_rope_append(a, D, p->q_mode, p->kv_dtype, stream);
     return e == hipSuccess ? QKPREP_OK : QKPREP_E_LAUNCH;
@@ -242,6 +244,7 @@ qkprep_status qkprep_mla_concat_rope_append(const qkprep_mla_params* p, hipStrea
     a.chunks_per_token = (a.H + 15) / 16 + 1;
     a.tokens_per_tile = kMaxTokensPerTile;
     a.total_items = (int64_t)T * a.chunks_per_token;
+    if (a.total_items > INT32_MAX) return QKPREP_E_SHAPE;
     hipError_t e = q8 ? launch_mla_q8(a, p->kv_dtype, stream) : launch_mla_concat_rope(a, p->kv_dtype, stream);
     return e == hipSuccess ? QKPREP_OK : QKPREP_E_LAUNCH;
 }

@@ -121,6 +121,8 @@ def _status(p):
     (dict(kv_dtype=1, kv_scale_mode=2, kv_group_size=32, rotary_dim=64, k_scale_out=0x10000,
           v_scale_out=0x11000), 3),
     (dict(kv_dtype=1, k_scale=None, v_scale=None), 1),
+    # more (token, chunk) items than 32-bit item indices reach
+    (dict(num_tokens=(1 << 31) - 1), 2),
 ])
 def test_host_checks_reject_before_launch(over, expect):
     assert _status(_params(**over)) == expect
