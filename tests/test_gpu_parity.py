@@ -207,11 +207,28 @@ def test_dynamic_kv_scales(D, mode, g, addressing):
     run_and_compare(inp)
 
 
-@pytest.mark.parametrize("R", [64, 0])
-def test_token_kv_scales_with_partial_rotary(R):
-    q, prior = _ragged(R + 5, B=4, max_q=30, max_prior=100)
-    inp = W.nra_case(seed=R + 5, q_lens=q, prior_lens=prior, Hq=4, Hkv=4, D=128, page_size=8,
+@pytest.mark.parametrize("D,R", [(128, 64), (128, 0), (128, 96), (128, 112), (64, 32), (256, 192)])
+def test_token_kv_scales_with_partial_rotary(D, R):
+    """Per-token K/V scales (an amax over the whole K row) with every
+    rotary load layout: mirrored halves, the outer-lane trade above half the
+    head, and paired rows of 64-dim heads."""
+    q, prior = _ragged(R + D + 5, B=4, max_q=30, max_prior=100)
+    inp = W.nra_case(seed=R + D + 5, q_lens=q, prior_lens=prior, Hq=4, Hkv=4, D=D, page_size=8,
                      rotary_dim=R, kv_fp8=True, kv_scale_mode=W.KV_SCALE_TOKEN)
+    run_and_compare(inp)
+
+
+@pytest.mark.parametrize("D,R", [(128, 96), (64, 48), (256, 208)])
+@pytest.mark.parametrize("q_mode", [W.Q_FP8_STATIC, W.Q_BF16])
+def test_wide_partial_rotary_other_q_modes(D, R, q_mode):
+    """Rotary above half the head (and 64-dim partial rotary) with static
+    E4M3 Q and bf16 Q, interleaved pairs, Gemma weights, K written back in
+    place for the bf16 arm."""
+    q, prior = _ragged(R + D + 11, B=5, max_q=25, max_prior=150)
+    bf = q_mode == W.Q_BF16
+    inp = W.nra_case(seed=R + D + 11, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=D, page_size=16,
+                     rotary_dim=R, rope=W.ROPE_INTERLEAVED, norm=W.NORM_GEMMA, q_mode=q_mode, q_scale_inv=2.0,
+                     kv_fp8=not bf, k_scale=0.05, v_scale=0.05, q_in_place=bf, k_in_place=bf)
     run_and_compare(inp)
 
 
