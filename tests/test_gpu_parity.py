@@ -311,15 +311,17 @@ def test_slot_addressing(kv_fp8):
     run_and_compare(inp)
 
 
-def test_long_call_with_slot_addressing():
+@pytest.mark.parametrize("D,R", [(128, 128), (128, 96), (128, 32), (64, 32)])
+def test_long_call_with_slot_addressing(D, R):
     """Over 8 tokens per resident workgroup the kernel deals 4-token spans
     round-robin instead of one contiguous range per workgroup: slot
     addressing, per-token-head Q scales, padding slots and suppressed
-    positions on that path."""
+    positions on that path, with the whole-head and the partial-rotary load
+    layouts."""
     q_lens = np.array([3001, 2999, 3100, 17], np.int64)
-    inp = W.nra_case(seed=23, q_lens=q_lens, prior_lens=np.array([5, 0, 64, 900]), Hq=8, Hkv=2, D=128,
+    inp = W.nra_case(seed=23 + R, q_lens=q_lens, prior_lens=np.array([5, 0, 64, 900]), Hq=8, Hkv=2, D=D,
                      page_size=16, addressing=W.ADDR_SLOT, q_mode=W.Q_FP8_DYNAMIC, kv_fp8=True,
-                     k_scale=0.05, v_scale=0.05, rope=W.ROPE_INTERLEAVED)
+                     k_scale=0.05, v_scale=0.05, rope=W.ROPE_INTERLEAVED, rotary_dim=R)
     assert inp.T >= 8 * 1024
     inp.slot_mapping = inp.slot_mapping.copy()
     inp.slot_mapping[[0, 4097, inp.T - 1]] = -1
