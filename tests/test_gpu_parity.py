@@ -377,9 +377,17 @@ def test_empty_call_launches_nothing():
 @pytest.mark.parametrize("mutation", ["first_nonzero", "non_monotone", "last_short", "seq_len_below_q_len",
                                       "too_many_pages", "page_id_negative", "page_id_past_pool",
                                       "above_max_seqlen"])
-def test_malformed_metadata(mutation):
-    q, prior = _ragged(31)
-    q[0] = 5
+@pytest.mark.parametrize("shape", ["ragged", "short"])
+def test_malformed_metadata(mutation, shape):
+    """Each malformed input rejects the whole call: on a ragged batch (full
+    validation path) and on a batch of 1-2-token requests, which writes at
+    most two pages per request (short validation path)."""
+    if shape == "ragged":
+        q, prior = _ragged(31)
+        q[0] = 5
+    else:
+        q = np.array([2, 1, 2, 1, 1, 2, 1, 1, 2, 1, 1, 1], np.int64)
+        prior = np.random.default_rng(32).integers(0, 100, size=len(q))
     inp = W.nra_case(seed=31, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=16,
                      q_mode=W.Q_FP8_DYNAMIC, q_scale_padded=True, max_seqlen=64, kv_fp8=True,
                      k_scale=0.05, v_scale=0.05)
@@ -390,7 +398,7 @@ def test_malformed_metadata(mutation):
     elif mutation == "last_short":
         inp.q_indptr[-1] = inp.T - 1
     elif mutation == "seq_len_below_q_len":
-        inp.seq_lens[0] = 2
+        inp.seq_lens[0] = int(q[0]) - 1
     elif mutation == "too_many_pages":
         inp.seq_lens[3] = inp.page_table.shape[1] * inp.page_size + 1
     elif mutation == "page_id_negative":
@@ -398,7 +406,7 @@ def test_malformed_metadata(mutation):
     elif mutation == "page_id_past_pool":
         inp.page_table[2, (int(inp.seq_lens[2]) - 1) // inp.page_size] = inp.num_pages
     elif mutation == "above_max_seqlen":
-        inp.max_seqlen = 4
+        inp.max_seqlen = int(q.max()) - 1
     dev = H.DeviceNra(inp)
     dev.run()
     torch.cuda.synchronize()
