@@ -304,10 +304,13 @@ static int nra_invalid(const oracle_nra_args *a)
         if (sl < qlen) return 1;
         if (sl > (int64_t)a->maxp * a->page_size) return 1;
         if (a->q_mode == 1 && a->q_scale_padded && qlen > a->max_seqlen) return 1;
-        /* pages this call addresses: the appended rows, and the last page
-         * if its tail is cleared (never when K/V are redirected) */
+        /* page ids are checked for the pages this call writes: the
+         * appended rows' pages, and the last page if its tail is cleared.
+         * With K/V redirected to out_k / out_v the call writes no page, so
+         * no page id is checked (and none is read). */
+        if (a->out_k) continue;
         int64_t first_row = sl - qlen;
-        if (a->zero_tail && !a->out_k && qlen == 0 && sl > 0) first_row = sl - 1;
+        if (a->zero_tail && qlen == 0 && sl > 0) first_row = sl - 1;
         for (int64_t L = first_row; L < sl; ++L) {
             int32_t p = a->page_table[(int64_t)b * a->maxp + L / a->page_size];
             if (p < 0 || p >= a->num_pages) return 1;
@@ -476,7 +479,8 @@ int oracle_norm_rope_append(const oracle_nra_args *a)
                 if (position_out_of_table(a, t)) continue;
                 int64_t pos = a->rot ? a->positions[t] : 0;
                 int64_t L = sl - qlen + j;            /* logical row in the request */
-                int64_t page = a->page_table[(int64_t)b * a->maxp + L / a->page_size];
+                /* (redirected K/V rows are addressed by token: no page is read) */
+                int64_t page = a->out_k ? -1 : a->page_table[(int64_t)b * a->maxp + L / a->page_size];
                 nra_token(a, t, b, j, pos, page, L % a->page_size);
             }
         }

@@ -403,9 +403,19 @@ def test_mla_concat_layout_and_values(fp8):
     inp = W.mla_case(seed=3, T=9, H=4, num_blocks=4, block_size=8, kv_fp8=fp8, negative_slots=2)
     out = run_mla(inp)
     K, R, nope = inp.kv_lora_rank, inp.rope_dim, inp.nope_dim
-    # q_nope untouched, q_rope changed
+    # q_nope untouched; each head's rope slice is the interleaved rotation of
+    # that head's own slice by the token's own angles, written as bf16 (numpy
+    # complex multiplication of the pairs (2i, 2i+1) by cos + i sin, in fp64)
     assert np.array_equal(out["q"][:, :, :nope], inp.q[:, :, :nope])
-    assert (out["q"][:, :, nope:] != inp.q[:, :, nope:]).mean() > 0.9
+    for t in range(inp.T):
+        pos = inp.positions[t]
+        e = inp.cos_sin[pos, :R // 2].astype(np.float64) + 1j * inp.cos_sin[pos, R // 2:].astype(np.float64)
+        for h in range(inp.H):
+            x = W.bf16_bits_to_f32(inp.q[t, h, nope:]).astype(np.float64)
+            z = (x[0::2] + 1j * x[1::2]) * e
+            o = np.empty(R)
+            o[0::2], o[1::2] = z.real, z.imag
+            assert np.array_equal(out["q"][t, h, nope:], W.to_bf16_bits(o.astype(np.float32))), (t, h)
     written = set()
     for t in range(inp.T):
         s = int(inp.slot_mapping[t])
@@ -564,6 +574,31 @@ def test_redirected_kv_rows_equal_the_cache_rows_and_leave_the_caches_alone(kv_f
             crow = page * plain.page_size + row
             assert np.array_equal(orr["k_scale_out"][t], op["k_scale_out"][crow])
             assert np.array_equal(orr["v_scale_out"][t], op["v_scale_out"][crow])
+
+
+@pytest.mark.parametrize("mutation", ["page_id_negative", "page_id_past_pool"])
+def test_redirect_reads_and_checks_no_page_id(mutation):
+    """Page ids are checked for the pages a call writes (the FlashInfer
+    contract's validation guards the pool; its review: nothing is written
+    into the caches when K/V are redirected).  A redirected call writes no
+    page, so an out-of-pool page id leaves it valid with the same outputs,
+    while the same table makes the paged call invalid.  The other metadata
+    checks still apply under redirect."""
+    kw = dict(kv_fp8=True, k_scale=0.05, v_scale=0.07, q_mode=W.Q_FP8_DYNAMIC)
+    ok = run_oracle(_small(kv_redirect=True, **kw))
+    red = _small(kv_redirect=True, **kw)
+    _mutations()[mutation](red)
+    got = run_oracle(red)
+    assert (got["flags"] == 0).all()
+    for k in ("q_out", "out_k", "out_v", "k_cache", "v_cache"):
+        assert np.array_equal(got[k], ok[k]), k
+    plain = _small(**kw)
+    _mutations()[mutation](plain)
+    assert (run_oracle(plain)["flags"] == -1).all()
+    bad_len = _small(kv_redirect=True, **kw)
+    _mutations()["seq_len_below_q_len"](bad_len)
+    out = run_oracle(bad_len)
+    assert (out["flags"] == -1).all() and np.array_equal(out["out_k"], bad_len.out_k0)
 
 
 def test_token_kv_scales_closed_forms():
