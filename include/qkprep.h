@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QKPREP_ABI_VERSION 1
+#define QKPREP_ABI_VERSION 2
 
 typedef enum {
     QKPREP_OK = 0,
@@ -80,6 +80,17 @@ typedef enum {
                                       /* row length P = round_up(max_seqlen, 128)             */
 } qkprep_qscale_layout;
 typedef enum { QKPREP_ADDR_PAGED = 0, QKPREP_ADDR_SLOT = 1 } qkprep_addressing;
+/* Cache policy for the rows a call writes (token rows of Q, K and V, the MLA
+ * latent rows and the E4M3 MLA query).  Not on the pages, which leave the
+ * store path open; a choice of this library, measured on MI355X. */
+typedef enum {
+    QKPREP_STORE_STREAM = 0,   /* default: non-temporal stores, so that the written rows drain
+                                  to HBM as they are produced instead of occupying L2 and the
+                                  Infinity Cache; rows written back into qkv (in-place Q / K)
+                                  keep ordinary stores */
+    QKPREP_STORE_KEEP = 1      /* ordinary stores everywhere: the rows stay in L2 / the
+                                  Infinity Cache for a kernel that reads them right after */
+} qkprep_store_policy;
 typedef enum {
     QKPREP_KV_SCALE_STATIC = 0,    /* device scalars k_scale / v_scale */
     QKPREP_KV_SCALE_TOKEN = 1,     /* dynamic, one per (token, kv head) */
@@ -207,6 +218,8 @@ typedef struct qkprep_norm_rope_append_params {
     int32_t kv_group_size;
     float* k_scale_out;
     float* v_scale_out;
+
+    int32_t store_policy;          /* qkprep_store_policy (0 = QKPREP_STORE_STREAM) */
 } qkprep_norm_rope_append_params;
 
 /*
@@ -273,6 +286,9 @@ typedef struct qkprep_mla_params {
     float* q_scale;                /* FP8_DYNAMIC: fp32 [T] */
     const float* q_scale_inv;      /* FP8_STATIC: device fp32 scalar */
     float upper_max;               /* FP8_DYNAMIC: finite, in (0, 448] */
+
+    int32_t store_policy;          /* qkprep_store_policy (0 = QKPREP_STORE_STREAM; the in-place
+                                      q rope slices follow it too) */
 } qkprep_mla_params;
 
 /* Host checks, then one kernel launch on `stream` (none when there is no

@@ -8,7 +8,7 @@ provides device memory and streams.
 """
 from .binding import (  # noqa: F401
     ADDR_PAGED, ADDR_SLOT, BF16, FP8_E4M3, KV_SCALE_GROUP, KV_SCALE_STATIC, KV_SCALE_TOKEN, NORM_GEMMA, NORM_NONE, NORM_RMS, QSCALE_REQ_HEAD_PADDED,
-    QSCALE_TOKEN_HEAD, Q_BF16, Q_FP8_DYNAMIC, Q_FP8_STATIC, ROPE_INTERLEAVED, ROPE_NEOX, LIB_PATH,
+    QSCALE_TOKEN_HEAD, Q_BF16, STORE_KEEP, STORE_STREAM, Q_FP8_DYNAMIC, Q_FP8_STATIC, ROPE_INTERLEAVED, ROPE_NEOX, LIB_PATH,
     MlaParams, NormRopeAppendParams, QkprepError, call_mla_concat_rope_append, call_norm_rope_append,
     lib, mla_params, norm_rope_append_params, qkprep_abi_version, qkprep_mla_concat_rope_append,
     qkprep_norm_rope_append, qkprep_status_string,

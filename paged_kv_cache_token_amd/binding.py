@@ -26,6 +26,7 @@ ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 Q_BF16, Q_FP8_DYNAMIC, Q_FP8_STATIC = 0, 1, 2
 KV_SCALE_STATIC, KV_SCALE_TOKEN, KV_SCALE_GROUP = 0, 1, 2
 QSCALE_TOKEN_HEAD, QSCALE_REQ_HEAD_PADDED = 0, 1
+STORE_STREAM, STORE_KEEP = 0, 1
 ADDR_PAGED, ADDR_SLOT = 0, 1
 
 _vp = ctypes.c_void_p
@@ -54,6 +55,7 @@ class NormRopeAppendParams(ctypes.Structure):
         ("flags", _vp),
         ("out_k", _vp), ("out_v", _vp), ("out_kv_row_stride", _i64),
         ("kv_scale_mode", _i32), ("kv_group_size", _i32), ("k_scale_out", _vp), ("v_scale_out", _vp),
+        ("store_policy", _i32),
     ]
 
 
@@ -71,6 +73,7 @@ class MlaParams(ctypes.Structure):
         ("block_stride", _i64), ("kv_scale", _vp),
         ("q_mode", _i32), ("q_out", _vp), ("q_out_token_stride", _i64), ("q_out_head_stride", _i64),
         ("q_scale", _vp), ("q_scale_inv", _vp), ("upper_max", ctypes.c_float),
+        ("store_policy", _i32),
     ]
 
 
@@ -154,7 +157,7 @@ def norm_rope_append_params(*, qkv, num_q_heads, num_kv_heads, head_dim, cos_sin
                             num_tokens=None, qkv_row_stride=None, num_requests=None,
                             rotary_dim=None, out_k=None, out_v=None, out_kv_row_stride=None,
                             kv_scale_mode=KV_SCALE_STATIC, kv_group_size=0, k_scale_out=None,
-                            v_scale_out=None) -> NormRopeAppendParams:
+                            v_scale_out=None, store_policy=STORE_STREAM) -> NormRopeAppendParams:
     """Fill the params struct from tensors (shapes/strides read from them when not given).
 
     The struct holds raw device pointers; it also keeps a reference to every
@@ -208,6 +211,7 @@ def norm_rope_append_params(*, qkv, num_q_heads, num_kv_heads, head_dim, cos_sin
         p.out_kv_row_stride = out_k.stride(0) if out_kv_row_stride is None else out_kv_row_stride
     p.kv_scale_mode, p.kv_group_size = kv_scale_mode, kv_group_size
     p.k_scale_out, p.v_scale_out = _ptr(k_scale_out), _ptr(v_scale_out)
+    p.store_policy = store_policy
     return p
 
 
@@ -227,7 +231,7 @@ def mla_params(*, q, kv_c, k_pe, cos_sin_cache, positions, slot_mapping, kv_cach
                nope_dim=128, rope_dim=64, kv_lora_rank=512, rope=ROPE_INTERLEAVED, kv_dtype=FP8_E4M3,
                kv_scale=None, num_tokens=None, q_token_stride=None, q_head_stride=None, q_mode=Q_BF16,
                q_out=None, q_out_token_stride=None, q_out_head_stride=None, q_scale=None, q_scale_inv=None,
-               upper_max=448.0) -> MlaParams:
+               upper_max=448.0, store_policy=STORE_STREAM) -> MlaParams:
     """Fill the MLA params struct from tensors; like norm_rope_append_params,
     the struct keeps a reference to every tensor it points into."""
     p = MlaParams()
@@ -252,6 +256,7 @@ def mla_params(*, q, kv_c, k_pe, cos_sin_cache, positions, slot_mapping, kv_cach
         p.q_out_token_stride = q_out.stride(0) if q_out_token_stride is None else q_out_token_stride
         p.q_out_head_stride = q_out.stride(1) if q_out_head_stride is None else q_out_head_stride
     p.q_scale, p.q_scale_inv, p.upper_max = _ptr(q_scale), _ptr(q_scale_inv), upper_max
+    p.store_policy = store_policy
     return p
 
 

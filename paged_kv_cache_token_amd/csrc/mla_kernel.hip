@@ -83,7 +83,7 @@ struct MlaCursor {
     }
 };
 
-template <bool KVFP8>
+template <bool KVFP8, bool NT>
 __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) {
     constexpr int U = kBatch;
     typedef typename std::conditional<KVFP8, uint8_t, uint16_t>::type kv_t;
@@ -203,8 +203,8 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
                     mirror_exchange<kDppRowHalfMirror, 0xA, 0x5>(lo, hi);
                     const int ha = chunk * kHeadsPerWave + (grp & ~1), hb = ha + 1;
                     uint16_t* q = a.q + (int64_t)t * a.q_token_stride + a.nope_dim;
-                    if (pos >= 0 && ha < a.H) st16(q + (int64_t)ha * a.q_head_stride + q_off0, lo);
-                    if (pos >= 0 && hb < a.H) st16(q + (int64_t)hb * a.q_head_stride + q_off1, hi);
+                    if (pos >= 0 && ha < a.H) st16p<NT>(q + (int64_t)ha * a.q_head_stride + q_off0, lo);
+                    if (pos >= 0 && hb < a.H) st16p<NT>(q + (int64_t)hb * a.q_head_stride + q_off1, hi);
                 } else {
                     // k_pe second halves come from lanes 4..7 (all lanes take part)
                     const uint4 pe = buf[u][1];
@@ -219,9 +219,9 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
                         if constexpr (KVFP8) {
                             float x[8];
                             unpack8(buf[u][0], x);
-                            st8(dst + 8 * lane, pack8_fp8(x, inv_scale));
+                            st8p<NT>(dst + 8 * lane, pack8_fp8(x, inv_scale));
                         } else {
-                            st16(dst + 8 * lane, buf[u][0]);
+                            st16p<NT>(dst + 8 * lane, buf[u][0]);
                         }
                         // latent ranks past the first 512 (kv_lora_rank = 1024, ...)
                         for (int e = 512 + 8 * lane; e < K; e += 512) {
@@ -229,9 +229,9 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
                             if constexpr (KVFP8) {
                                 float x[8];
                                 unpack8(v, x);
-                                st8(dst + e, pack8_fp8(x, inv_scale));
+                                st8p<NT>(dst + e, pack8_fp8(x, inv_scale));
                             } else {
-                                st16(dst + e, v);
+                                st16p<NT>(dst + e, v);
                             }
                         }
                         if (lane < kLanesPerHead) {
@@ -241,11 +241,11 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
                             unpack8(pe_hi, x + 8);
                             rope16(x, c, s, a.rope);
                             if constexpr (KVFP8) {
-                                store_fp8_row(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf, pack8_fp8(x, inv_scale),
+                                store_fp8_row<NT>(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf, pack8_fp8(x, inv_scale),
                                               pack8_fp8(x + 8, inv_scale));
                             } else {
-                                st16(dst + K + 8 * gl, pack8_bf16(x));
-                                st16(dst + K + kHalf + 8 * gl, pack8_bf16(x + 8));
+                                st16p<NT>(dst + K + 8 * gl, pack8_bf16(x));
+                                st16p<NT>(dst + K + kHalf + 8 * gl, pack8_bf16(x + 8));
                             }
                         }
                     }
@@ -272,30 +272,16 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     }
 }
 
-template <bool KVFP8>
-int resident_blocks() {
-    static int cached_dev = -1, cached = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev != cached_dev) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mla_kernel<KVFP8>, kBlockThreads, 0) != hipSuccess)
-            per_cu = 1;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-        cached = (per_cu < 1 ? 1 : per_cu) * cus;
-        cached_dev = dev;
-    }
-    return cached;
-}
-
-template <bool KVFP8>
+template <bool KVFP8, bool NT>
 hipError_t launch_t(const MlaDevArgs& a, hipStream_t stream) {
     MlaDevArgs la = a;
-    const int64_t cap = resident_blocks<KVFP8>();
+    int64_t cap = resident_grid(reinterpret_cast<const void*>(&mla_kernel<KVFP8, NT>), 0);
+    if (cap < 1) cap = 256;
     int64_t want = (a.total_items + 7) / 8;
     if (want < 1) want = 1;
     la.grid = (int)(want < cap ? want : cap);
-    hipLaunchKernelGGL((mla_kernel<KVFP8>), dim3(la.grid), dim3(kBlockThreads), 0, stream, la);
+    (void)hipGetLastError();   // the status below then covers this launch only
+    hipLaunchKernelGGL((mla_kernel<KVFP8, NT>), dim3(la.grid), dim3(kBlockThreads), 0, stream, la);
     return hipGetLastError();
 }
 
@@ -317,7 +303,7 @@ hipError_t launch_t(const MlaDevArgs& a, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 constexpr int kQ8Rounds = 2;
 
-template <int QMODE, bool KVFP8>
+template <int QMODE, bool KVFP8, bool NT>
 __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs a) {
     typedef typename std::conditional<KVFP8, uint8_t, uint16_t>::type kv_t;
     __shared__ float s_amax[2][4];
@@ -418,7 +404,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                             float x[16];
                             unpack8(vn[k][j], x);
                             unpack8(vn[k][j + 1], x + 8);
-                            store_fp8_row(oh + 32 * j, gl, 32, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
+                            store_fp8_row<NT>(oh + 32 * j, gl, 32, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
                         }
                     }
                 } else {
@@ -427,11 +413,11 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                         if (j < NV) {
                             float x[8];
                             unpack8(vn[k][j], x);
-                            st8(oh + 8 * (gl + 4 * j), pack8_fp8(x, mul));
+                            st8p<NT>(oh + 8 * (gl + 4 * j), pack8_fp8(x, mul));
                         }
                     }
                 }
-                store_fp8_row(oh + N, gl, kHalf, pack8_fp8(xr[k], mul), pack8_fp8(xr[k] + 8, mul));
+                store_fp8_row<NT>(oh + N, gl, kHalf, pack8_fp8(xr[k], mul), pack8_fp8(xr[k] + 8, mul));
             }
         }
 
@@ -447,18 +433,18 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                 if constexpr (KVFP8) {
                     float x[8];
                     unpack8(kvv, x);
-                    st8(dst + 8 * lane, pack8_fp8(x, 1.0f / kv_scale_v));
+                    st8p<NT>(dst + 8 * lane, pack8_fp8(x, 1.0f / kv_scale_v));
                 } else {
-                    st16(dst + 8 * lane, kvv);
+                    st16p<NT>(dst + 8 * lane, kvv);
                 }
                 for (int e = 512 + 8 * lane; e < K; e += 512) {
                     const uint4 v = ld16(a.kv_c + t * a.kv_c_stride + e);
                     if constexpr (KVFP8) {
                         float x[8];
                         unpack8(v, x);
-                        st8(dst + e, pack8_fp8(x, 1.0f / kv_scale_v));
+                        st8p<NT>(dst + e, pack8_fp8(x, 1.0f / kv_scale_v));
                     } else {
-                        st16(dst + e, v);
+                        st16p<NT>(dst + e, v);
                     }
                 }
                 if (lane < kLanesPerHead) {
@@ -467,11 +453,11 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
                     unpack8(pe_hi, x + 8);
                     rope16(x, c, s, a.rope);
                     if constexpr (KVFP8) {
-                        store_fp8_row(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf,
+                        store_fp8_row<NT>(reinterpret_cast<uint8_t*>(dst + K), gl, kHalf,
                                       pack8_fp8(x, 1.0f / kv_scale_v), pack8_fp8(x + 8, 1.0f / kv_scale_v));
                     } else {
-                        st16(dst + K + 8 * gl, pack8_bf16(x));
-                        st16(dst + K + kHalf + 8 * gl, pack8_bf16(x + 8));
+                        st16p<NT>(dst + K + 8 * gl, pack8_bf16(x));
+                        st16p<NT>(dst + K + kHalf + 8 * gl, pack8_bf16(x + 8));
                     }
                 }
             }
@@ -479,41 +465,32 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
     }
 }
 
-template <int QMODE, bool KVFP8>
-int q8_resident_blocks() {
-    static int cached_dev = -1, cached = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev != cached_dev) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mla_q8_kernel<QMODE, KVFP8>, kBlockThreads, 0) !=
-            hipSuccess)
-            per_cu = 1;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-        cached = (per_cu < 1 ? 1 : per_cu) * cus;
-        cached_dev = dev;
-    }
-    return cached;
-}
-
-template <int QMODE, bool KVFP8>
+template <int QMODE, bool KVFP8, bool NT>
 hipError_t launch_q8_t(const MlaDevArgs& a, hipStream_t stream) {
     MlaDevArgs la = a;
-    const int64_t cap = q8_resident_blocks<QMODE, KVFP8>();
+    int64_t cap = resident_grid(reinterpret_cast<const void*>(&mla_q8_kernel<QMODE, KVFP8, NT>), 0);
+    if (cap < 1) cap = 256;
     la.grid = (int)(a.T < cap ? a.T : cap);
-    hipLaunchKernelGGL((mla_q8_kernel<QMODE, KVFP8>), dim3(la.grid), dim3(kBlockThreads), 0, stream, la);
+    (void)hipGetLastError();   // the status below then covers this launch only
+    hipLaunchKernelGGL((mla_q8_kernel<QMODE, KVFP8, NT>), dim3(la.grid), dim3(kBlockThreads), 0, stream, la);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mla_concat_rope(const MlaDevArgs& a, int kv_fp8, hipStream_t stream) {
-    return kv_fp8 ? launch_t<true>(a, stream) : launch_t<false>(a, stream);
+    if (a.nt_store) return kv_fp8 ? launch_t<true, true>(a, stream) : launch_t<false, true>(a, stream);
+    return kv_fp8 ? launch_t<true, false>(a, stream) : launch_t<false, false>(a, stream);
 }
 
 hipError_t launch_mla_q8(const MlaDevArgs& a, int kv_fp8, hipStream_t stream) {
-    if (a.q_mode == 1) return kv_fp8 ? launch_q8_t<1, true>(a, stream) : launch_q8_t<1, false>(a, stream);
-    return kv_fp8 ? launch_q8_t<2, true>(a, stream) : launch_q8_t<2, false>(a, stream);
+    const bool nt = a.nt_store != 0;
+    if (a.q_mode == 1) {
+        if (nt) return kv_fp8 ? launch_q8_t<1, true, true>(a, stream) : launch_q8_t<1, false, true>(a, stream);
+        return kv_fp8 ? launch_q8_t<1, true, false>(a, stream) : launch_q8_t<1, false, false>(a, stream);
+    }
+    if (nt) return kv_fp8 ? launch_q8_t<2, true, true>(a, stream) : launch_q8_t<2, false, true>(a, stream);
+    return kv_fp8 ? launch_q8_t<2, true, false>(a, stream) : launch_q8_t<2, false, false>(a, stream);
 }
 
 }  // namespace qkprep

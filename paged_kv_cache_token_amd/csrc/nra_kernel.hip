@@ -90,6 +90,9 @@ __device__ __forceinline__ ReqPages request_pages(const NraDevArgs& a, const int
         r.bad = 1;
         return r;
     }
+    // page ids are checked for the pages the call writes; K/V redirected to
+    // out_k / out_v write no page, so none is read or checked
+    if (a.redirect) return r;
     int lo_row = sl - ql;
     if (a.zero_tail && ql == 0 && sl > 0) lo_row = sl - 1;
     if (sl > lo_row) {
@@ -248,6 +251,7 @@ __device__ __forceinline__ LaneMap lane_map(int rot, int gl) {
 // E4M3 codes of the lane's two pieces (lo at o0, hi at o1) into a head row
 // of bytes.  Paired rope lanes trade one 8-byte half so that each writes 16
 // contiguous bytes: the even lane [o0, o0 + 16), the odd lane [o1 - 8, o1 + 8).
+template <bool NT>
 __device__ __forceinline__ void store_fp8_lane(uint8_t* row, int gl, const LaneMap& m, uint2 lo, uint2 hi) {
     const bool odd = gl & 1;
     const uint2 send = odd ? lo : hi;
@@ -260,10 +264,10 @@ __device__ __forceinline__ void store_fp8_lane(uint8_t* row, int gl, const LaneM
         const bool swap = m.fp8_store == 1;
         const uint4 v = !swap ? make_uint4(lo.x, lo.y, hi.x, hi.y)
                         : odd ? make_uint4(recv.x, recv.y, hi.x, hi.y) : make_uint4(lo.x, lo.y, recv.x, recv.y);
-        st16(row + ((swap && odd) ? m.o1 - 8 : m.o0), v);
+        st16p<NT>(row + ((swap && odd) ? m.o1 - 8 : m.o0), v);
     } else {
-        st8(row + m.o0, lo);
-        st8(row + m.o1, hi);
+        st8p<NT>(row + m.o0, lo);
+        st8p<NT>(row + m.o1, hi);
     }
 }
 
@@ -328,7 +332,7 @@ struct RowConsts {
     float* s_qs;     // non-null: stage dynamic Q scales in LDS [token][head]
 };
 
-template <int D, int QMODE, bool KVFP8>
+template <int D, int QMODE, bool KVFP8, bool NT>
 __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, int r, int gl, const LaneMap& lm,
                                             uint4 v0, uint4 v1, const float* s_w, const float* s_cs_row,
                                             const int64_t* s_koff, const int64_t* s_voff, const int64_t* s_qsoff,
@@ -352,10 +356,10 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
                 lo = pack8_fp8(x, k.inv_v);
                 hi = pack8_fp8(x + 8, k.inv_v);
             }
-            store_fp8_lane(reinterpret_cast<uint8_t*>(row), gl, lm, lo, hi);
+            store_fp8_lane<NT>(reinterpret_cast<uint8_t*>(row), gl, lm, lo, hi);
         } else {
-            st16(row + lm.o0, v0);
-            st16(row + lm.o1, v1);
+            st16p<NT>(row + lm.o0, v0);
+            st16p<NT>(row + lm.o1, v1);
         }
         return;
     }
@@ -430,8 +434,8 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
         const int h = r;
         if constexpr (QMODE == 0) {
             uint16_t* row = reinterpret_cast<uint16_t*>(a.q_out) + (int64_t)t * a.q_out_stride + h * D;
-            st16(row + lm.o0, pack8_bf16(x));
-            st16(row + lm.o1, pack8_bf16(x + 8));
+            st16p<NT>(row + lm.o0, pack8_bf16(x));
+            st16p<NT>(row + lm.o1, pack8_bf16(x + 8));
         } else {
             uint8_t* row = reinterpret_cast<uint8_t*>(a.q_out) + (int64_t)t * a.q_out_stride + h * D;
             if constexpr (QMODE == 1) {
@@ -447,10 +451,10 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
                     if (k.s_qs) k.s_qs[ti * a.Hq + h] = sc;
                     else a.q_scale[s_qsoff[ti] + (int64_t)h * k.qs_hstride] = sc;
                 }
-                store_fp8_lane(row, gl, lm, pack8_fp8_bounded(x, mul), pack8_fp8_bounded(x + 8, mul));
+                store_fp8_lane<NT>(row, gl, lm, pack8_fp8_bounded(x, mul), pack8_fp8_bounded(x + 8, mul));
             } else {
                 const float mul = f * k.q_static;
-                store_fp8_lane(row, gl, lm, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
+                store_fp8_lane<NT>(row, gl, lm, pack8_fp8(x, mul), pack8_fp8(x + 8, mul));
             }
         }
     } else {
@@ -466,16 +470,16 @@ __device__ __forceinline__ void process_row(const NraDevArgs& a, int t, int ti, 
                     lo = pack8_fp8(x, f * k.inv_k);
                     hi = pack8_fp8(x + 8, f * k.inv_k);
                 }
-                store_fp8_lane(reinterpret_cast<uint8_t*>(row), gl, lm, lo, hi);
+                store_fp8_lane<NT>(reinterpret_cast<uint8_t*>(row), gl, lm, lo, hi);
             } else {
-                st16(row + lm.o0, pack8_bf16(x));
-                st16(row + lm.o1, pack8_bf16(x + 8));
+                st16p<NT>(row + lm.o0, pack8_bf16(x));
+                st16p<NT>(row + lm.o1, pack8_bf16(x + 8));
             }
         }
         if (a.k_out) {
             uint16_t* ko = a.k_out + (int64_t)t * a.k_out_stride + kh * D;
-            st16(ko + lm.o0, pack8_bf16(x));
-            st16(ko + lm.o1, pack8_bf16(x + 8));
+            st16p<NT>(ko + lm.o0, pack8_bf16(x));
+            st16p<NT>(ko + lm.o1, pack8_bf16(x + 8));
         }
     }
 }
@@ -492,9 +496,11 @@ struct Cursor {
     }
 };
 
-template <int D, int QMODE, bool KVFP8, int ROT, bool STREAM>
+template <int D, int QMODE, bool KVFP8, int ROT, int MEM>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4))) void nra_kernel(const NraDevArgs a) {
     constexpr bool PART = ROT == kRotPart;
+    constexpr bool NTL = MEM != kMemInPlace;     // qkv read once: streaming loads
+    constexpr bool NTS = MEM == kMemStream;      // token rows: streaming stores
     constexpr int G = D / 16;        // lanes per head row
     constexpr int RPW = 64 / G;      // head rows per wave
     constexpr int U = kBatch;
@@ -630,7 +636,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
                 const int ra = ld.c * RPW + (grp & ~1), rb = ra + 1;
                 const uint16_t* sa = tok + ((ld.left > 0 && ra < a.R) ? ra : 0) * D + ld_o0;
                 const uint16_t* sb = tok + ((ld.left > 0 && rb < a.R) ? rb : 0) * D + ld_o1;
-                if constexpr (STREAM) {
+                if constexpr (NTL) {
                     buf[u][0] = ld16_stream(sa);
                     buf[u][1] = ld16_stream(sb);
                 } else {
@@ -644,7 +650,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
             const bool ok = ld.left > 0 && r < a.R;
             const int rr = ok ? r : 0;
             const uint16_t* src = tok + rr * D;
-            if constexpr (STREAM) {
+            if constexpr (NTL) {
                 buf[u][0] = ld16_stream(src + ld_o0);
                 buf[u][1] = ld16_stream(src + ld_o1);
             } else {
@@ -929,7 +935,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
                 const int r = pr.c * RPW + grp;
                 const int ti = pr.t - t_first;
                 if (r < a.R && s_pos[ti] >= 0)
-                    process_row<D, QMODE, KVFP8>(a, pr.t, ti, r, gl, lm, buf[u][0], buf[u][1], s_w,
+                    process_row<D, QMODE, KVFP8, NTS>(a, pr.t, ti, r, gl, lm, buf[u][0], buf[u][1], s_w,
                                                  s_cs + ti * D, s_koff, s_voff, s_qsoff, s_srow, kc);
                 pr.advance(CPT);
             }
@@ -1033,36 +1039,15 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
 
 }
 
-// workgroups per CU the kernel can keep resident (queried once per device)
-template <int D, int QMODE, bool KVFP8, int ROT, bool STREAM>
-int resident_blocks(size_t lds) {
-    static int cached_dev = -1, cached = 0, cached_cus = 0;
-    static size_t cached_lds = (size_t)-1;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (dev != cached_dev || lds != cached_lds) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nra_kernel<D, QMODE, KVFP8, ROT, STREAM>, kBlockThreads,
-                                                         lds) != hipSuccess)
-            per_cu = 1;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
-        cached = (per_cu < 1 ? 1 : per_cu) * cus;
-        cached_cus = cus;
-        cached_dev = dev;
-        cached_lds = lds;
-    }
-    (void)cached_cus;
-    return cached;
-}
-
-template <int D, int QMODE, bool KVFP8, int ROT, bool STREAM>
+template <int D, int QMODE, bool KVFP8, int ROT, int MEM>
 hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     size_t lds = a.paged ? (size_t)(3 * a.B + 2) * sizeof(int) : 0;
     if (a.stage_q_scale) lds = (size_t)((3 * a.B + 2 + 3) & ~3) * sizeof(int) + (size_t)kMaxTokensPerTile * a.Hq * sizeof(float);
     // enough workgroups to fill every CU, none with less than 8 head-row
     // chunks of work, and at least one per request when tails are cleared
     // (one per 4 requests otherwise, for the flags)
-    const int64_t cap = resident_blocks<D, QMODE, KVFP8, ROT, STREAM>(lds);
+    int64_t cap = resident_grid(reinterpret_cast<const void*>(&nra_kernel<D, QMODE, KVFP8, ROT, MEM>), lds);
+    if (cap < 1) cap = 256;
     // 8 (token, chunk) items per workgroup, but 4 for small calls (up to 64
     // workgroups): a tiny decode's time is its latency chain, which more
     // workgroups shorten (16 tokens: 9.4 -> 8.1 us), while at B = 256 the
@@ -1096,7 +1081,8 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     // 15k-token prefill gains about 2 us).  Other layouts keep the plain
     // round-robin, which measured faster for them in steady state.
     la.xcd_spans = (la.interleave > 0 && a.stage_q_scale && la.grid % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, ROT, STREAM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
+    (void)hipGetLastError();   // the status below then covers this launch only
+    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, ROT, MEM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();
 }
 
@@ -1109,26 +1095,29 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
 #define QKPREP_CAT(x, y) QKPREP_CAT2(x, y)
 
 // Launch for head dim QKPREP_NRA_HEAD_DIM: picks the instance for the Q mode,
-// the cache dtype, the rotary layout (whole head, partial, none) and
-// streaming or cached qkv loads.  A call without rotated dims takes the
+// the cache dtype, the rotary layout (whole head, partial, none) and the
+// memory mode (in place: cached loads and stores; streaming loads with
+// streaming or ordinary row stores).  A call without rotated dims takes the
 // whole-head lane layout, whose load instructions read whole lines.
 hipError_t QKPREP_CAT(launch_norm_rope_append_d, QKPREP_NRA_HEAD_DIM)(const NraDevArgs& a, int q_mode, int kv_fp8,
                                                                        hipStream_t stream) {
     constexpr int D = QKPREP_NRA_HEAD_DIM;
+#define QKPREP_NRA_ROT(QM, KF, RT)                                                                       \
+    switch (a.mem) {                                                                                     \
+        case kMemInPlace: return launch_t<D, QM, KF, RT, kMemInPlace>(a, stream);                          \
+        case kMemStream: return launch_t<D, QM, KF, RT, kMemStream>(a, stream);                            \
+        default: return launch_t<D, QM, KF, RT, kMemKeep>(a, stream);                                      \
+    }
 #define QKPREP_NRA_CASE(QM, KF)                                                                          \
     if (q_mode == QM && (kv_fp8 != 0) == KF) {                                                           \
-        if (a.rot == D)                                                                                  \
-            return a.stream_qkv ? launch_t<D, QM, KF, kRotWhole, true>(a, stream)                         \
-                                : launch_t<D, QM, KF, kRotWhole, false>(a, stream);                       \
-        if (a.rot == 0)                                                                                  \
-            return a.stream_qkv ? launch_t<D, QM, KF, kRotNone, true>(a, stream)                          \
-                                : launch_t<D, QM, KF, kRotNone, false>(a, stream);                        \
-        return a.stream_qkv ? launch_t<D, QM, KF, kRotPart, true>(a, stream)                              \
-                            : launch_t<D, QM, KF, kRotPart, false>(a, stream);                            \
+        if (a.rot == D) QKPREP_NRA_ROT(QM, KF, kRotWhole)                                                \
+        if (a.rot == 0) QKPREP_NRA_ROT(QM, KF, kRotNone)                                                 \
+        QKPREP_NRA_ROT(QM, KF, kRotPart)                                                                 \
     }
     QKPREP_NRA_CASE(0, false) QKPREP_NRA_CASE(0, true)
     QKPREP_NRA_CASE(1, false) QKPREP_NRA_CASE(1, true)
     QKPREP_NRA_CASE(2, false) QKPREP_NRA_CASE(2, true)
+#undef QKPREP_NRA_ROT
 #undef QKPREP_NRA_CASE
     return hipErrorInvalidValue;
 }

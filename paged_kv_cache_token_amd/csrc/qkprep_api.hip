@@ -8,6 +8,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 #include "qkprep.h"
 #include "qkprep_internal.h"
 
@@ -17,7 +20,43 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+struct ResidentEntry {
+    const void* kernel;
+    int device;
+    size_t lds;
+    int grid;
+};
+
 }  // namespace
+
+namespace qkprep {
+
+int resident_grid(const void* kernel, size_t dyn_lds) {
+    static std::mutex mu;
+    static std::vector<ResidentEntry> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const ResidentEntry& e : cache)
+            if (e.kernel == kernel && e.device == dev && e.lds == dyn_lds) return e.grid;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlockThreads, dyn_lds) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int grid = (per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
+    std::lock_guard<std::mutex> lock(mu);
+    cache.push_back(ResidentEntry{kernel, dev, dyn_lds, grid});
+    return grid;
+}
+
+}  // namespace qkprep
 
 extern "C" {
 
@@ -50,6 +89,7 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
         p->q_scale_layout < 0 || p->q_scale_layout > 1)
         return QKPREP_E_RANGE;
     if (p->page_size <= 0) return QKPREP_E_RANGE;
+    if (p->store_policy < 0 || p->store_policy > 1) return QKPREP_E_RANGE;
     const bool redirect = p->out_k != nullptr || p->out_v != nullptr;
     if (redirect && (!p->out_k || !p->out_v)) return QKPREP_E_NULL;
     if (p->kv_scale_mode < 0 || p->kv_scale_mode > 2) return QKPREP_E_RANGE;
@@ -167,8 +207,10 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     a.q_scale_inv = p->q_scale_inv;
     a.upper_max = p->upper_max;
     a.k_out = static_cast<uint16_t*>(p->k_out);
-    // qkv rows are read once unless Q or K is written back into them
-    a.stream_qkv = (p->q_out != p->qkv && p->k_out == nullptr) ? 1 : 0;
+    // qkv rows are read once unless Q or K is written back into them; the
+    // rows written back keep ordinary stores (measured faster there)
+    const bool in_place = p->q_out == p->qkv || p->k_out != nullptr;
+    a.mem = in_place ? kMemInPlace : (p->store_policy == QKPREP_STORE_KEEP ? kMemKeep : kMemStream);
     a.k_out_stride = p->k_out_row_stride;
     a.flags = p->flags;
     const int rows_per_wave = 64 / (D / 16);
@@ -192,6 +234,7 @@ qkprep_status qkprep_mla_concat_rope_append(const qkprep_mla_params* p, hipStrea
     if (p->rope < 0 || p->rope > 1 || p->kv_dtype < 0 || p->kv_dtype > 1) return QKPREP_E_RANGE;
     if (p->block_size <= 0) return QKPREP_E_RANGE;
     if (p->q_mode < 0 || p->q_mode > 2) return QKPREP_E_RANGE;
+    if (p->store_policy < 0 || p->store_policy > 1) return QKPREP_E_RANGE;
     const bool q8 = p->q_mode != QKPREP_Q_BF16;
     if (q8 && (p->nope_dim % 32 || p->nope_dim > 128)) return QKPREP_E_UNSUPPORTED;
     if (p->q_mode == QKPREP_Q_FP8_DYNAMIC) {
@@ -241,6 +284,7 @@ qkprep_status qkprep_mla_concat_rope_append(const qkprep_mla_params* p, hipStrea
     a.q_out = static_cast<uint8_t*>(p->q_out);
     a.q_out_token_stride = p->q_out_token_stride; a.q_out_head_stride = p->q_out_head_stride;
     a.q_scale = p->q_scale; a.q_scale_inv = p->q_scale_inv; a.upper_max = p->upper_max;
+    a.nt_store = p->store_policy == QKPREP_STORE_KEEP ? 0 : 1;
     a.chunks_per_token = (a.H + 15) / 16 + 1;
     a.tokens_per_tile = kMaxTokensPerTile;
     a.total_items = (int64_t)T * a.chunks_per_token;

@@ -68,6 +68,33 @@ __device__ __forceinline__ void st8(void* p, uint2 v) {
     *reinterpret_cast<uint2*>(p) = v;
 }
 
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void st8_stream(void* p, uint2 v) {
+    typedef __attribute__((address_space(1))) u32x2_t gT;
+    const u32x2_t w = {v.x, v.y};
+    __builtin_nontemporal_store(w, (gT*)p);
+}
+
+// Row stores under the call's store policy: non-temporal (NT) for rows
+// written to outputs no kernel of this call reads back, so that they drain
+// to HBM as they are produced (with the previous calls' outputs still dirty
+// in the caches, ordinary stores left the rows waiting in L2 and cost the
+// 15k-token FP8 prefill about 8 % in steady state); ordinary stores when the
+// caller keeps the rows in the caches for the next kernel, or when they are
+// written back into lines the call has just read.
+template <bool NT>
+__device__ __forceinline__ void st16p(void* p, uint4 v) {
+    if constexpr (NT) st16_stream(p, v);
+    else st16(p, v);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st8p(void* p, uint2 v) {
+    if constexpr (NT) st8_stream(p, v);
+    else st8(p, v);
+}
+
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float4 ldf4(const float* p) {
@@ -327,6 +354,7 @@ __device__ __forceinline__ int block_or4(int v, int* slot) {
 // 8-byte half so that even lanes store dims [8 gl, 8 gl + 16) and odd lanes
 // dims [half + 8 gl - 8, half + 8 gl + 8): one 16-byte store per lane, and
 // the group writes whole 128-byte lines.
+template <bool NT>
 __device__ __forceinline__ void store_fp8_row(uint8_t* row, int gl, int half, uint2 lo, uint2 hi) {
     const bool odd = gl & 1;
     const uint2 send = odd ? lo : hi;
@@ -334,7 +362,7 @@ __device__ __forceinline__ void store_fp8_row(uint8_t* row, int gl, int half, ui
     recv.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.x, kDppQuadSwap1, 0xF, 0xF, false);
     recv.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send.y, kDppQuadSwap1, 0xF, 0xF, false);
     const uint4 v = odd ? make_uint4(recv.x, recv.y, hi.x, hi.y) : make_uint4(lo.x, lo.y, recv.x, recv.y);
-    st16(row + (odd ? half + 8 * (gl - 1) : 8 * gl), v);
+    st16p<NT>(row + (odd ? half + 8 * (gl - 1) : 8 * gl), v);
 }
 
 }  // namespace qkprep

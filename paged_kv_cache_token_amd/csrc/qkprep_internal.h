@@ -40,6 +40,11 @@ inline FastDiv31 make_fastdiv31(uint32_t d) {
     return f;
 }
 
+// Memory modes of the norm-rope-append kernel: Q or K written back into
+// qkv (cached loads and stores); qkv read once with streaming loads, and the
+// token rows stored with streaming (non-temporal) or ordinary stores.
+enum : int { kMemInPlace = 0, kMemStream = 1, kMemKeep = 2 };
+
 struct NraDevArgs {
     // shapes
     int32_t T, Hq, Hkv, R;             // R = Hq + 2 Hkv head rows per token
@@ -93,7 +98,7 @@ struct NraDevArgs {
     int32_t kv_group;
     float* k_scale_out;
     float* v_scale_out;
-    int32_t stream_qkv;                 // 1: qkv is read once (no Q/K written back): streaming loads
+    int32_t mem;                        // kMemInPlace / kMemStream / kMemKeep
     int32_t interleave;                 // items per round-robin span, 0 = one range per workgroup
     int32_t xcd_spans;                  // spans of a round grouped by XCD (blockIdx % 8)
     int32_t grid;                       // workgroups launched (set by the launcher)
@@ -124,12 +129,20 @@ struct MlaDevArgs {
     float* q_scale;
     const float* q_scale_inv;
     float upper_max;
+    int32_t nt_store;                   // 1: streaming (non-temporal) row stores
     // geometry: balanced contiguous ranges of the T * chunks_per_token items
     int32_t tokens_per_tile;            // most tokens staged in LDS at once
     int32_t chunks_per_token;           // ceil(H / heads per wave) + 1 latent chunk
     int64_t total_items;
     int32_t grid;                       // workgroups launched (set by the launcher)
 };
+
+// Workgroups of kBlockThreads threads that `kernel` keeps resident on the
+// current device with `dyn_lds` bytes of dynamic LDS, over all CUs.  Queried
+// once per (kernel, device, dyn_lds) and cached; safe to call from several
+// host threads.  Returns 0 if the device cannot be queried (a failed query's
+// error is cleared, so that it is not taken for a launch error).
+int resident_grid(const void* kernel, size_t dyn_lds);
 
 // returns hipSuccess or the launch error
 // one object of nra_kernel.hip per head dim

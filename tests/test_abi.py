@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
-    assert qp.qkprep_abi_version() == 1
+    assert qp.qkprep_abi_version() == 2
 
 
 @pytest.mark.parametrize("cname,pyclass", [("qkprep_norm_rope_append_params", B.NormRopeAppendParams),
@@ -123,6 +123,9 @@ def _status(p):
     (dict(kv_dtype=1, k_scale=None, v_scale=None), 1),
     # more (token, chunk) items than 32-bit item indices reach
     (dict(num_tokens=(1 << 31) - 1), 2),
+    # store policy: 0 streaming, 1 keep
+    (dict(store_policy=2), 5),
+    (dict(store_policy=-1), 5),
 ])
 def test_host_checks_reject_before_launch(over, expect):
     assert _status(_params(**over)) == expect
@@ -176,6 +179,8 @@ def test_mla_host_checks():
     assert st(q_mode=2, **dict(q8, q_out_head_stride=200)) == 4
     assert st(q_mode=2, **dict(q8, q_out=0x9008)) == 4
     assert st(q_mode=1, num_tokens=0, upper_max=448.0, q=None, **q8) == 0
+    assert st(store_policy=2) == 5
+    assert st(store_policy=-1) == 5
 
 
 def test_status_strings():
