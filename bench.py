@@ -5,32 +5,47 @@ One step = one pass of the whole norm-rope-append path over one batch of
 each workload the headline metric names:
   * decode, B = 256 requests x 1 token, Hq/Hkv/D 32/8/128, bf16 Q and bf16
     paged cache (page 16) over the full ~262k-page pool, tails cleared;
-  * ragged FP8 prefill, 8 requests (~15k tokens), 64/8/128, dynamic
-    per-token-head Q scales, E4M3 cache (page 64), tails cleared.
+  * ragged FP8 prefill of 16 384 tokens (8 requests, lengths in [1, 4096]),
+    64/8/128, dynamic per-token-head Q scales, E4M3 cache (page 64), tails
+    cleared.
 Inputs are seeded and synthetic and already resident in HBM when the timed
 region starts.  `value` is the step's algorithmic bytes (qkv read + norm
 weights + cos/sin rows + Q write incl. q_scale + cache write incl. tail
 zeros) divided by the measured step time, in GB/s (1e9 B/s).
 
-The timed region holds only the K steps' launches (no event markers
-between them: on this GPU each marker delays the next kernel by a few
-microseconds).  Also reported: tokens/s; each kernel's duration from HIP
-events on its launch stream around runs of back-to-back launches of that
-kernel (the roofline of the dominant kernel, the prefill launch, uses it);
-the same launches timed one at a time after a clean 512 MiB read flush of
-L2 and the 256 MB Infinity Cache; and the CPU oracle timed on the host on
-the same step.
+Cache protocol.  Every workload is held in several complete, independent
+copies ("sets": inputs, outputs, metadata, tables; the decode sets share the
+17 GB cache pool but write disjoint random pages), at least 4 of them and
+more than 1 GiB of touched memory in all, and consecutive launches take
+consecutive sets.  A launch then finds neither its inputs nor the previous
+launches' outputs in L2 or the 256 MB Infinity Cache, and the previous
+launches' dirty output lines are written back to HBM while it runs: the
+steady state of a serving loop.  The timed steps rotate the same way.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+Per-kernel timing (the roofline): 20 warm-up launches of each kernel, then
+3 sessions of 200 launches, each session timing a back-to-back run of
+rotating launches of each kernel with one HIP event pair on the launch
+stream (no marker between launches: on this GPU an event marker delays the
+next kernel by several microseconds); the kernel order alternates between
+sessions.  Also reported, as extra keys: the same kernel back-to-back on one
+set (its previous outputs still in the Infinity Cache), and single launches
+after a 512 MiB read flush or a 512 MiB write flush (events around each
+launch, so those figures include the launch latency).
+
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
        python bench.py --suite      (every configuration and variant, one by one)
        python bench.py --pages-rows (the FlashInfer PR's measured rows, beside its figures)
+       python bench.py --summarize-trace kernel_trace.csv --plan plan.json
+                                    (per-phase kernel durations from a rocprofv3 trace)
 """
 from __future__ import annotations
 
 import argparse
+import copy
 import ctypes
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -40,36 +55,43 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (% of MI355X peak) + tokens/s, decode B=256 and prefill 16k tok"
 HBM_PEAK_GBS = 8000.0
+# rotating sets: at least 4, and more than 1 GiB of touched memory in all
+SET_TARGET_BYTES = int(1.1 * (1 << 30))
+MIN_SETS, MAX_SETS = 4, 128
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--roofline-launches", type=int, default=20)
-    ap.add_argument("--kernel-launches", type=int, default=20,
-                    help="back-to-back launches per run when timing each kernel alone")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sessions", type=int, default=3)
+    ap.add_argument("--session-launches", type=int, default=200,
+                    help="rotating launches of each kernel per session")
+    ap.add_argument("--flush-launches", type=int, default=50,
+                    help="single launches after a read flush and after a write flush (extra keys)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-roofline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "mla"], default=None,
-                    help="time one workload alone (profiling runs)")
+    ap.add_argument("--only", choices=["decode", "prefill", "prefill_draw", "mla"], default=None,
+                    help="time one workload alone (counter runs)")
+    ap.add_argument("--plan-out", default=None,
+                    help="write the ordered list of library launches (workload, phase, count) as JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB copy (counter calibration) and exit")
     ap.add_argument("--suite", action="store_true",
                     help="time every workload (the five configurations and the variant rows) one by one "
                          "and print one JSON object; no headline line")
     ap.add_argument("--suite-only", default=None, help="comma-separated subset of the suite's workloads")
-    ap.add_argument("--suite-launches", type=int, default=200,
-                    help="clean-cache launches per session (three sessions) of each suite workload")
     ap.add_argument("--pages-rows", action="store_true",
                     help="time the FlashInfer PR's measured rows, rebuilt, after a cache flush each, and "
                          "print them beside that PR's B200 / H100 latencies (context only)")
-    return ap.parse_args()
+    ap.add_argument("--summarize-trace", default=None,
+                    help="rocprofv3 kernel_trace.csv to summarise per phase (needs --plan); no GPU")
+    ap.add_argument("--plan", default=None, help="launch plan written by --plan-out")
+    return ap.parse_args(argv)
 
 
 # Latencies in us that the FlashInfer PR (fused QK RMSNorm + NeoX RoPE + FP8
@@ -90,65 +112,394 @@ PAGES_ROW_US = {
 }
 
 
-def run_pages_rows(args, dev):
-    """Each of the PR's rows, rebuilt: 20 warm-up launches, then three
-    sessions of --suite-launches launches, each after a clean 512 MiB read
-    flush (HIP events around each launch)."""
-    import torch
-    import workloads as W
-    stream = torch.cuda.current_stream()
-    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    table = {}
-    for name in W.PAGES_ROWS:
-        log(f"pages row: {name}")
-        inp = W.pages_row(name, host_caches=False)
-        c = Call(inp, dev)
-        for _ in range(20):
-            c.launch()
-        torch.cuda.synchronize()
-        sessions = []
-        for _ in range(3):
-            cold = []
-            for _ in range(args.suite_launches):
-                flush.sum()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                c.launch()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                cold.append(e0.elapsed_time(e1) * 1e3)
-            sessions.append(sorted(cold))
-        allc = sorted(x for ses in sessions for x in ses)
-        med = percentile(allc, 0.5)
-        model = c.bytes - inp.algorithmic_bytes()["norm_weights"]
-        b200, h100 = PAGES_ROW_US[name]
-        table[name] = {"tokens": inp.T, "bytes_MB": round(model / 1e6, 3),
-                       "clean_cache_median_us": round(med, 2),
-                       "clean_cache_p10_us": round(percentile(allc, 0.1), 2),
-                       "clean_cache_p90_us": round(percentile(allc, 0.9), 2),
-                       "clean_cache_session_medians_us": [round(percentile(ses, 0.5), 2) for ses in sessions],
-                       "TBps": round(model / med / 1e6, 3),
-                       "pages_B200_us": b200, "pages_H100_us": h100}
-        log(f"  {table[name]}")
-        del c
-        torch.cuda.empty_cache()
-    print(json.dumps({"pages_rows": table, "launches_per_row": 3 * args.suite_launches}), flush=True)
+def percentile(sorted_vals, q):
+    """q-quantile (0..1) of an ascending list, by linear interpolation."""
+    if not sorted_vals:
+        return None
+    x = q * (len(sorted_vals) - 1)
+    i = int(x)
+    j = min(i + 1, len(sorted_vals) - 1)
+    return sorted_vals[i] + (sorted_vals[j] - sorted_vals[i]) * (x - i)
 
+
+# ---------------------------------------------------------------------------
+# launch plan: the ordered library launches, for matching a kernel trace
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Ordered (workload, phase, count) runs of library launches."""
+
+    def __init__(self):
+        self.runs = []
+
+    def add(self, name, phase, n=1):
+        if self.runs and self.runs[-1][0] == name and self.runs[-1][1] == phase:
+            self.runs[-1][2] += n
+        else:
+            self.runs.append([name, phase, n])
+
+    def dump(self, path):
+        with open(path, "w") as f:
+            json.dump({"runs": self.runs}, f)
+
+
+PLAN = Plan()
+
+
+def summarize_trace(csv_path, plan_path):
+    """Per-phase duration statistics of the library's kernels in a rocprofv3
+    kernel trace, matched in launch order against the plan bench.py wrote.
+    Prints one markdown table."""
+    import csv
+    with open(plan_path) as f:
+        runs = json.load(f)["runs"]
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name", "")
+            if "nra_kernel" in name or "mla_kernel" in name or "mla_q8_kernel" in name:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), name))
+    rows.sort()
+    want = sum(n for _, _, n in runs)
+    if len(rows) != want:
+        raise SystemExit(f"trace holds {len(rows)} library launches, the plan {want}")
+    out = {}
+    k = 0
+    for wl, phase, n in runs:
+        key = (wl, phase)
+        d = out.setdefault(key, {"durs": [], "kernel": rows[k][2]})
+        d["durs"] += [(e - s) / 1e3 for s, e, _ in rows[k:k + n]]
+        k += n
+    print("| workload | phase | launches | mean us | median us | p10 us | p90 us | kernel |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (wl, phase), d in out.items():
+        v = sorted(d["durs"])
+        kname = d["kernel"]
+        for stem in ("nra_kernel", "mla_q8_kernel", "mla_kernel"):
+            if stem in kname:
+                kname = kname[kname.index(stem):]
+                break
+        kname = kname.split("(")[0]
+        print(f"| {wl} | {phase} | {len(v)} | {sum(v) / len(v):.2f} | {percentile(v, 0.5):.2f} | "
+              f"{percentile(v, 0.1):.2f} | {percentile(v, 0.9):.2f} | `{kname}` |")
+
+
+# ---------------------------------------------------------------------------
+# device-resident calls and their rotating sets
+# ---------------------------------------------------------------------------
+
+def _seeded(dev, nbytes, seed, dt, shape):
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev).random_(0, 256, generator=g).view(dt).view(shape)
+
+
+class Call:
+    """Device-resident inputs and outputs of one norm-rope-append call."""
+
+    def __init__(self, inp, dev):
+        import numpy as np
+        import torch
+        import paged_kv_cache_token_amd as qp
+        import workloads as W
+        self.inp = inp
+        self.dev = dev
+
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(dt)
+
+        cdt = torch.uint8 if inp.kv_fp8 else torch.int16
+        cbytes = int(np.prod(inp.cache_shape)) * inp.kv_elt
+        self.qkv = up(inp.qkv, torch.int16)
+        if inp.k_cache0 is None:
+            self.k_cache = _seeded(dev, cbytes, inp.cache_seed, cdt, inp.cache_shape)
+            self.v_cache = _seeded(dev, cbytes, inp.cache_seed + 1, cdt, inp.cache_shape)
+        else:
+            self.k_cache = up(inp.k_cache0, cdt).view(inp.cache_shape)
+            self.v_cache = up(inp.v_cache0, cdt).view(inp.cache_shape)
+        qdt = torch.int16 if inp.q_mode == W.Q_BF16 else torch.uint8
+        self.q_out = self.qkv if inp.q_in_place else up(inp.q_out0, qdt)
+        self.q_scale = None if inp.q_scale0 is None else up(inp.q_scale0, torch.float32)
+        self.flags = up(inp.flags0, torch.int32)
+        extra = {}
+        if inp.kv_redirect:
+            extra.update(out_k=up(inp.out_k0, cdt), out_v=up(inp.out_v0, cdt))
+        if inp.kv_scale_mode:
+            extra.update(k_scale_out=up(inp.k_scale_out0, torch.float32),
+                         v_scale_out=up(inp.v_scale_out0, torch.float32))
+        sc = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)  # noqa: E731
+        self.t = dict(
+            qkv=self.qkv, q_norm_weight=up(inp.q_norm_weight, torch.float32),
+            k_norm_weight=up(inp.k_norm_weight, torch.float32), cos_sin_cache=up(inp.cos_sin, torch.float32),
+            positions=up(inp.positions, torch.int64), q_indptr=up(inp.q_indptr, torch.int32),
+            seq_lens=up(inp.seq_lens, torch.int32), page_table=up(inp.page_table, torch.int32),
+            k_cache=self.k_cache, v_cache=self.v_cache, k_scale=sc(inp.k_scale), v_scale=sc(inp.v_scale),
+            q_out=self.q_out, q_scale_inv=sc(inp.q_scale_inv), q_scale=self.q_scale, flags=self.flags, **extra)
+        self.bytes = inp.algorithmic_bytes()["total"]
+        self._finish()
+
+    def _finish(self):
+        import torch
+        import paged_kv_cache_token_amd as qp
+        inp = self.inp
+        k_out = None
+        if inp.k_in_place:
+            k_out = self.t["qkv"].view(-1)[inp.Hq * inp.D:].as_strided((inp.T, inp.Hkv * inp.D),
+                                                                       (inp.qkv_row_stride, 1))
+        kw = dict(self.t)
+        kw.update(
+            num_q_heads=inp.Hq, num_kv_heads=inp.Hkv, head_dim=inp.D, norm=inp.norm, eps=inp.eps, rope=inp.rope,
+            kv_dtype=qp.FP8_E4M3 if inp.kv_fp8 else qp.BF16, zero_tail=1 if inp.zero_tail else 0,
+            q_out_row_stride=inp.qkv_row_stride if inp.q_in_place else inp.Hq * inp.D, q_mode=inp.q_mode,
+            k_out=k_out, k_out_row_stride=inp.qkv_row_stride, qkv_row_stride=inp.qkv_row_stride,
+            num_tokens=inp.T,
+            q_scale_layout=qp.QSCALE_REQ_HEAD_PADDED if inp.q_scale_padded else qp.QSCALE_TOKEN_HEAD,
+            max_seqlen=inp.max_seqlen, upper_max=inp.upper_max, rotary_dim=inp.rot,
+            kv_scale_mode=inp.kv_scale_mode, kv_group_size=inp.kv_group_size, store_policy=inp.store_policy)
+        self.params = qp.norm_rope_append_params(**kw)
+        self.params.struct_size = ctypes.sizeof(self.params)
+        self._ref = ctypes.byref(self.params)
+        self._fn = qp.lib().qkprep_norm_rope_append
+        self._stream = torch.cuda.current_stream().cuda_stream
+
+    def clone(self, idx):
+        """An independent copy (another set) of this call's device memory.
+        A call whose cache pool was filled on the device (the 17 GB decode
+        pool) shares that pool; its page table is remapped through a seeded
+        permutation of the pool, so the copy writes other pages."""
+        import numpy as np
+        import torch
+        c = copy.copy(self)
+        c.t = {}
+        for k, v in self.t.items():
+            c.t[k] = v
+        shared_pool = self.inp.k_cache0 is None
+        for k, v in self.t.items():
+            if v is None or (shared_pool and k in ("k_cache", "v_cache")):
+                continue
+            if k == "q_out" and self.inp.q_in_place:
+                continue
+            c.t[k] = v.clone()
+        if self.inp.q_in_place:
+            c.t["q_out"] = c.t["qkv"]
+        if shared_pool:
+            perm = torch.from_numpy(np.random.default_rng(7919 + idx).permutation(self.inp.num_pages)
+                                    .astype(np.int64)).to(self.dev)
+            pt = self.t["page_table"]
+            c.t["page_table"] = torch.where(pt >= 0, perm[pt.clamp(min=0).long()].to(torch.int32), pt)
+        c.qkv, c.q_out, c.q_scale, c.flags = c.t["qkv"], c.t["q_out"], c.t["q_scale"], c.t["flags"]
+        c.k_cache, c.v_cache = c.t["k_cache"], c.t["v_cache"]
+        c._finish()
+        return c
+
+    def launch(self):
+        st = self._fn(self._ref, self._stream)
+        if st != 0:
+            import paged_kv_cache_token_amd as qp
+            raise qp.QkprepError(st)
+
+
+class MlaCall:
+    def __init__(self, inp, dev):
+        import numpy as np
+        import torch
+        self.inp = inp
+        self.dev = dev
+
+        def up(a, dt):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(dt)
+        sc = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)  # noqa: E731
+        self.t = dict(
+            q=up(inp.q, torch.int16), kv_c=up(inp.kv_c, torch.int16), k_pe=up(inp.k_pe, torch.int16),
+            cos_sin_cache=up(inp.cos_sin, torch.float32), positions=up(inp.positions, torch.int64),
+            slot_mapping=up(inp.slot_mapping, torch.int64), kv_cache=up(inp.kv_cache0, torch.uint8),
+            kv_scale=sc(inp.kv_scale), q_out=None if inp.q_out0 is None else up(inp.q_out0, torch.uint8),
+            q_scale=None if inp.q_scale0 is None else up(inp.q_scale0, torch.float32),
+            q_scale_inv=sc(inp.q_scale_inv))
+        self.bytes = inp.algorithmic_bytes()["total"]
+        self._finish()
+
+    def _finish(self):
+        import torch
+        import paged_kv_cache_token_amd as qp
+        inp = self.inp
+        t = self.t
+        kv_cache = t["kv_cache"].view(inp.num_blocks, inp.block_size, -1)
+        # (the params struct keeps every tensor below alive)
+        self.params = qp.mla_params(
+            q=t["q"].view(inp.T, inp.H, -1), kv_c=t["kv_c"].view(inp.T, -1), k_pe=t["k_pe"].view(inp.T, -1),
+            cos_sin_cache=t["cos_sin_cache"].view(-1, inp.rope_dim), positions=t["positions"],
+            slot_mapping=t["slot_mapping"], kv_cache=kv_cache, num_q_heads=inp.H, nope_dim=inp.nope_dim,
+            kv_scale=t["kv_scale"], q_mode=inp.q_mode,
+            q_out=None if t["q_out"] is None else t["q_out"].view(inp.T, inp.H, -1),
+            q_scale=t["q_scale"], q_scale_inv=t["q_scale_inv"], upper_max=inp.upper_max,
+            store_policy=inp.store_policy)
+        self.params.struct_size = ctypes.sizeof(self.params)
+        self._ref = ctypes.byref(self.params)
+        self._fn = qp.lib().qkprep_mla_concat_rope_append
+        self._stream = torch.cuda.current_stream().cuda_stream
+
+    def clone(self, idx):
+        c = copy.copy(self)
+        c.t = {k: (None if v is None else v.clone()) for k, v in self.t.items()}
+        c._finish()
+        return c
+
+    def launch(self):
+        st = self._fn(self._ref, self._stream)
+        if st != 0:
+            import paged_kv_cache_token_amd as qp
+            raise qp.QkprepError(st)
+
+
+def n_sets(nbytes):
+    return int(min(MAX_SETS, max(MIN_SETS, math.ceil(SET_TARGET_BYTES / max(nbytes, 1)))))
+
+
+class Rotation:
+    """Rotating sets of one call: launch() takes the next set in turn."""
+
+    def __init__(self, name, base):
+        self.name = name
+        self.base = base
+        self.inp = base.inp
+        self.bytes = base.bytes
+        S = n_sets(base.bytes)
+        self.sets = [base] + [base.clone(i) for i in range(1, S)]
+        self.i = 0
+
+    @property
+    def touched_bytes(self):
+        return self.bytes * len(self.sets)
+
+    def launch(self, phase):
+        self.sets[self.i].launch()
+        self.i = (self.i + 1) % len(self.sets)
+        PLAN.add(self.name, phase)
+
+    def launch_same(self, phase):
+        self.sets[0].launch()
+        PLAN.add(self.name, phase)
+
+
+# ---------------------------------------------------------------------------
+# timing protocols
+# ---------------------------------------------------------------------------
+
+def _ev():
+    import torch
+    return torch.cuda.Event(enable_timing=True)
+
+
+def time_run(launch, n, stream):
+    """us per launch of a back-to-back run of n launches (one event pair)."""
+    import torch
+    e0, e1 = _ev(), _ev()
+    e0.record(stream)
+    for _ in range(n):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def time_single(launch, n, flush, stream):
+    """Sorted us of n single launches, each after flush() (events around the launch)."""
+    import torch
+    out = []
+    for _ in range(n):
+        flush()
+        e0, e1 = _ev(), _ev()
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3)
+    return sorted(out)
+
+
+class Flushes:
+    """512 MiB read flush (a sum) and 512 MiB write flush (a fill)."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        self.k = 0
+
+    def read(self):
+        self.buf.sum()
+
+    def write(self):
+        self.k += 1
+        self.buf.fill_(float(self.k & 255))
+
+
+def measure_arms(rots, args, stream, flushes):
+    """The roofline protocol over several kernels ("arms"): 20 warm-up
+    launches each, then args.sessions sessions of args.session_launches
+    rotating launches per arm, the arm order alternating between sessions;
+    then the extra modes (back-to-back on one set, single launches after a
+    read or a write flush)."""
+    import torch
+    names = list(rots)
+    for n in names:
+        for _ in range(20):
+            rots[n].launch("warmup")
+    torch.cuda.synchronize()
+    sess = {n: [] for n in names}
+    orders = []
+    for s in range(args.sessions):
+        order = names if s % 2 == 0 else names[::-1]
+        orders.append(list(order))
+        for n in order:
+            r = rots[n]
+            sess[n].append(time_run(lambda: r.launch(f"rotating_s{s + 1}"), args.session_launches, stream))
+    res = {}
+    for n in names:
+        r = rots[n]
+        same = sorted(time_run(lambda: r.launch_same("same_set"), 20, stream) for _ in range(3))
+        rf = time_single(lambda: r.launch_same("read_flush"), args.flush_launches, flushes.read, stream)
+        wf = time_single(lambda: r.launch_same("write_flush"), args.flush_launches, flushes.write, stream)
+        med = sorted(sess[n])[len(sess[n]) // 2]
+        res[n] = {
+            "tokens": r.inp.T, "algorithmic_bytes": r.bytes, "sets": len(r.sets),
+            "rotating_touched_MB": round(r.touched_bytes / 1e6, 1),
+            "rotating_us": round(med, 2), "rotating_session_us": [round(x, 2) for x in sess[n]],
+            "GBps": round(r.bytes / (med * 1e-6) / 1e9, 1),
+            "pct_of_peak": round(100 * r.bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "Mtok_per_s": round(r.inp.T / med, 2),
+            "same_set_back_to_back_us": round(same[1], 2),
+            "read_flush_median_us": round(percentile(rf, 0.5), 2),
+            "read_flush_p10_p90_us": [round(percentile(rf, 0.1), 2), round(percentile(rf, 0.9), 2)],
+            "write_flush_median_us": round(percentile(wf, 0.5), 2),
+            "write_flush_p10_p90_us": [round(percentile(wf, 0.1), 2), round(percentile(wf, 0.9), 2)],
+        }
+    return res, orders
+
+
+# ---------------------------------------------------------------------------
+# suite and pages rows
+# ---------------------------------------------------------------------------
 
 def suite_workloads():
     """Name -> (constructor, kind) of every timed workload: the five
     configurations, then the variants (partial rotary, 64-dim heads, MLA
-    with E4M3 Q, dynamic K/V scales, K/V redirect) at the prefill and MLA
-    shapes."""
+    with E4M3 Q, dynamic K/V scales, K/V redirect, small pages) at the
+    prefill and MLA shapes."""
     import workloads as W
     return {
         "c1_tiny_decode": (W.c1_tiny_decode, "nra"),
         "c2_decode_b256": (W.c2_decode_b256, "nra"),
         "c2_decode_b256_no_tail_clear": (lambda: W.c2_decode_b256(zero_tail=False), "nra"),
         "c3_prefill_fp8": (W.c3_prefill_fp8, "nra"),
+        "c3_prefill_fp8_16k": (W.c3_prefill_fp8_16k, "nra"),
         "c4_strided_d256": (W.c4_strided_d256, "nra"),
         "c5_mla": (W.c5_mla, "mla"),
+        "prefill_16k_page16": (lambda: W.c3_prefill_fp8_16k(page_size=16, maxp=256,
+                                                            name="prefill_16k_page16"), "nra"),
+        "prefill_16k_page1": (lambda: W.c3_prefill_fp8_16k(page_size=1, maxp=4096,
+                                                           name="prefill_16k_page1"), "nra"),
         "prefill_d64_gqa_64_8": (lambda: W.c3_prefill_fp8(D=64, name="prefill_d64"), "nra"),
         "prefill_rotary_64_of_128": (lambda: W.c3_prefill_fp8(rotary_dim=64, name="prefill_r64"), "nra"),
         "prefill_nope_layer": (lambda: W.c3_prefill_fp8(rotary_dim=0, name="prefill_r0"), "nra"),
@@ -164,183 +515,59 @@ def suite_workloads():
     }
 
 
-def percentile(sorted_vals, q):
-    """q-quantile (0..1) of an ascending list, by linear interpolation."""
-    if not sorted_vals:
-        return None
-    x = q * (len(sorted_vals) - 1)
-    i = int(x)
-    j = min(i + 1, len(sorted_vals) - 1)
-    return sorted_vals[i] + (sorted_vals[j] - sorted_vals[i]) * (x - i)
-
-
 def run_suite(args, dev):
-    """Each workload alone: 20 warm-up launches; three runs of 20
-    back-to-back launches (events on the launch stream around each run);
-    then three sessions of --suite-launches launches, each after a clean
-    512 MiB read flush of L2 and the Infinity Cache (events around each
-    launch): median, p10 and p90 over all of them and each session's median."""
+    """Each workload alone, in the roofline protocol (one arm)."""
     import torch
     table = {}
     names = list(suite_workloads())
     if args.suite_only:
         names = [n for n in args.suite_only.split(",") if n]
     stream = torch.cuda.current_stream()
-    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    n_clean = args.suite_launches
+    flushes = Flushes(dev)
     for name in names:
         make, kind = suite_workloads()[name]
         log(f"suite: {name}")
         inp = make()
-        c = MlaCall(inp, dev) if kind == "mla" else Call(inp, dev)
-        for _ in range(20):
-            c.launch()
-        torch.cuda.synchronize()
-        runs = []
-        for _ in range(3):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(20):
-                c.launch()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            runs.append(e0.elapsed_time(e1) * 1e3 / 20)
-        sessions = []
-        for _ in range(3):
-            cold = []
-            for _ in range(n_clean):
-                flush.sum()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                c.launch()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                cold.append(e0.elapsed_time(e1) * 1e3)
-            sessions.append(sorted(cold))
-        allc = sorted(x for ses in sessions for x in ses)
-        avg = sorted(runs)[1]
-        med = percentile(allc, 0.5)
-        table[name] = {"tokens": inp.T, "algorithmic_bytes": c.bytes, "avg_us": round(avg, 2),
-                       "back_to_back_runs_us": [round(r, 2) for r in runs],
-                       "clean_cache_median_us": round(med, 2),
-                       "clean_cache_p10_us": round(percentile(allc, 0.1), 2),
-                       "clean_cache_p90_us": round(percentile(allc, 0.9), 2),
-                       "clean_cache_session_medians_us": [round(percentile(ses, 0.5), 2) for ses in sessions],
-                       "clean_cache_launches": len(allc),
-                       "GBps": round(c.bytes / (avg * 1e-6) / 1e9, 1),
-                       "clean_cache_GBps": round(c.bytes / (med * 1e-6) / 1e9, 1),
-                       "clean_cache_pct_of_peak": round(100 * c.bytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                       "Mtok_per_s_clean": round(inp.T / med, 2)}
+        base = MlaCall(inp, dev) if kind == "mla" else Call(inp, dev)
+        rot = Rotation(name, base)
+        res, _ = measure_arms({name: rot}, args, stream, flushes)
+        table[name] = res[name]
         log(f"  {table[name]}")
-        del c
+        del rot, base
         torch.cuda.empty_cache()
-    print(json.dumps({"suite": table, "peak_GBps": HBM_PEAK_GBS}), flush=True)
+    print(json.dumps({"suite": table, "peak_GBps": HBM_PEAK_GBS, "sessions": args.sessions,
+                      "session_launches": args.session_launches}), flush=True)
 
 
-class Call:
-    """Device-resident inputs and outputs of one norm-rope-append call."""
-
-    def __init__(self, inp, dev):
-        import numpy as np
-        import torch
-        import paged_kv_cache_token_amd as qp
-        import workloads as W
-        self.inp = inp
-
-        def up(a, dt):
-            return torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(dt)
-
-        def seeded(nbytes, seed, dt, shape):
-            g = torch.Generator(device=dev)
-            g.manual_seed(seed)
-            return torch.empty(nbytes, dtype=torch.uint8, device=dev).random_(0, 256, generator=g).view(dt).view(shape)
-
-        cdt = torch.uint8 if inp.kv_fp8 else torch.int16
-        cbytes = int(np.prod(inp.cache_shape)) * inp.kv_elt
-        self.qkv = up(inp.qkv, torch.int16)
-        self.k_cache = seeded(cbytes, inp.cache_seed, cdt, inp.cache_shape)
-        self.v_cache = seeded(cbytes, inp.cache_seed + 1, cdt, inp.cache_shape)
-        qdt = torch.int16 if inp.q_mode == W.Q_BF16 else torch.uint8
-        self.q_out = self.qkv if inp.q_in_place else up(inp.q_out0, qdt)
-        k_out = None
-        if inp.k_in_place:
-            k_out = self.qkv.view(-1)[inp.Hq * inp.D:].as_strided((inp.T, inp.Hkv * inp.D),
-                                                                  (inp.qkv_row_stride, 1))
-        self.q_scale = None if inp.q_scale0 is None else up(inp.q_scale0, torch.float32)
-        self.flags = up(inp.flags0, torch.int32)
-        redirect = {}
-        if inp.kv_redirect:
-            redirect = dict(out_k=up(inp.out_k0, cdt), out_v=up(inp.out_v0, cdt))
-        scales = {}
-        if inp.kv_scale_mode:
-            scales = dict(k_scale_out=up(inp.k_scale_out0, torch.float32),
-                          v_scale_out=up(inp.v_scale_out0, torch.float32))
-        self.extra = dict(redirect, **scales)
-        sc = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)  # noqa: E731
-        self.kw = dict(
-            qkv=self.qkv, num_q_heads=inp.Hq, num_kv_heads=inp.Hkv, head_dim=inp.D, norm=inp.norm,
-            eps=inp.eps, q_norm_weight=up(inp.q_norm_weight, torch.float32),
-            k_norm_weight=up(inp.k_norm_weight, torch.float32), rope=inp.rope,
-            cos_sin_cache=up(inp.cos_sin, torch.float32), positions=up(inp.positions, torch.int64),
-            q_indptr=up(inp.q_indptr, torch.int32), seq_lens=up(inp.seq_lens, torch.int32),
-            page_table=up(inp.page_table, torch.int32), k_cache=self.k_cache, v_cache=self.v_cache,
-            kv_dtype=qp.FP8_E4M3 if inp.kv_fp8 else qp.BF16, k_scale=sc(inp.k_scale), v_scale=sc(inp.v_scale),
-            zero_tail=1 if inp.zero_tail else 0, q_out=self.q_out, q_out_row_stride=inp.qkv_row_stride if inp.q_in_place else inp.Hq * inp.D,
-            q_mode=inp.q_mode, k_out=k_out, k_out_row_stride=inp.qkv_row_stride, qkv_row_stride=inp.qkv_row_stride,
-            q_scale_inv=sc(inp.q_scale_inv), num_tokens=inp.T,
-            q_scale=self.q_scale,
-            q_scale_layout=qp.QSCALE_REQ_HEAD_PADDED if inp.q_scale_padded else qp.QSCALE_TOKEN_HEAD,
-            max_seqlen=inp.max_seqlen, upper_max=inp.upper_max, flags=self.flags, rotary_dim=inp.rot,
-            kv_scale_mode=inp.kv_scale_mode, kv_group_size=inp.kv_group_size, **self.extra)
-        self.params = qp.norm_rope_append_params(**self.kw)
-        self.params.struct_size = ctypes.sizeof(self.params)
-        self._ref = ctypes.byref(self.params)
-        self._fn = qp.lib().qkprep_norm_rope_append
-        self._stream = torch.cuda.current_stream().cuda_stream
-        self.bytes = inp.algorithmic_bytes()["total"]
-
-    def launch(self):
-        st = self._fn(self._ref, self._stream)
-        if st != 0:
-            import paged_kv_cache_token_amd as qp
-            raise qp.QkprepError(st)
+def run_pages_rows(args, dev):
+    """Each of the PR's rows, rebuilt, in the roofline protocol.  The
+    write-flush and read-flush single-launch figures are the closest to the
+    PR's cold-L2 kernel-activity medians (they include the launch latency;
+    the kernel trace of the same command gives the kernel time alone)."""
+    import torch
+    import workloads as W
+    stream = torch.cuda.current_stream()
+    flushes = Flushes(dev)
+    table = {}
+    for name in W.PAGES_ROWS:
+        log(f"pages row: {name}")
+        inp = W.pages_row(name, host_caches=False)
+        rot = Rotation(name, Call(inp, dev))
+        res, _ = measure_arms({name: rot}, args, stream, flushes)
+        r = res[name]
+        model = rot.bytes - inp.algorithmic_bytes()["norm_weights"]
+        b200, h100 = PAGES_ROW_US[name]
+        r.update({"bytes_MB": round(model / 1e6, 3), "pages_B200_us": b200, "pages_H100_us": h100})
+        table[name] = r
+        log(f"  {r}")
+        del rot
+        torch.cuda.empty_cache()
+    print(json.dumps({"pages_rows": table}), flush=True)
 
 
-class MlaCall:
-    def __init__(self, inp, dev):
-        import numpy as np
-        import torch
-        import paged_kv_cache_token_amd as qp
-        self.inp = inp
-
-        def up(a, dt):
-            return torch.from_numpy(np.ascontiguousarray(a)).to(dev).view(dt)
-        self.q = up(inp.q, torch.int16)
-        self.cache = up(inp.kv_cache0, torch.uint8)
-        sc = lambda x: torch.tensor([x], dtype=torch.float32, device=dev)  # noqa: E731
-        self.q_out = None if inp.q_out0 is None else up(inp.q_out0, torch.uint8)
-        self.q_scale = None if inp.q_scale0 is None else up(inp.q_scale0, torch.float32)
-        # (the params struct keeps every tensor below alive)
-        self.params = qp.mla_params(
-            q=self.q, kv_c=up(inp.kv_c, torch.int16), k_pe=up(inp.k_pe, torch.int16),
-            cos_sin_cache=up(inp.cos_sin, torch.float32), positions=up(inp.positions, torch.int64),
-            slot_mapping=up(inp.slot_mapping, torch.int64), kv_cache=self.cache, num_q_heads=inp.H,
-            nope_dim=inp.nope_dim, kv_scale=sc(inp.kv_scale), q_mode=inp.q_mode, q_out=self.q_out,
-            q_scale=self.q_scale, q_scale_inv=sc(inp.q_scale_inv), upper_max=inp.upper_max)
-        self.params.struct_size = ctypes.sizeof(self.params)
-        self._ref = ctypes.byref(self.params)
-        self._fn = qp.lib().qkprep_mla_concat_rope_append
-        self._stream = torch.cuda.current_stream().cuda_stream
-        self.bytes = inp.algorithmic_bytes()["total"]
-
-    def launch(self):
-        st = self._fn(self._ref, self._stream)
-        if st != 0:
-            import paged_kv_cache_token_amd as qp
-            raise qp.QkprepError(st)
-
+# ---------------------------------------------------------------------------
+# roofline bookkeeping and the CPU baseline
+# ---------------------------------------------------------------------------
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
@@ -350,14 +577,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "nra_prefill_fp8_16k_counters.txt")
+
+
 def recorded_traffic(kernel_hash: str):
-    """HBM bytes per launch of the prefill kernel from the committed rocprofv3
-    counter summary, valid only for the kernel source it was taken on."""
-    path = os.path.join(ROOT, "profiles", "nra_prefill_fp8_c3_counters.txt")
-    if not os.path.exists(path):
+    """Bytes per launch of the headline prefill kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE scaled by the copy
+    calibration), valid only for the kernel source it was taken on."""
+    if not os.path.exists(COUNTERS_FILE):
         return None
     vals = {}
-    with open(path) as f:
+    with open(COUNTERS_FILE) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -365,7 +595,7 @@ def recorded_traffic(kernel_hash: str):
     if vals.get("kernel_source_hash") != kernel_hash:
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -384,13 +614,13 @@ def host_cpu():
     return model, os.cpu_count()
 
 
-def cpu_baseline(c2, c3):
+def cpu_baseline(calls):
     """The oracle (single-threaded C, fp64) on the same step: the decode call
     on its touched pages and the full prefill call.  The step is timed three
     times (once if a run takes over 10 s) and the median reported."""
     runs = []
     while True:
-        t, nbytes, ntok = cpu_step(c2, c3)
+        t, nbytes, ntok = cpu_step(calls)
         runs.append(t)
         if len(runs) == 3 or t > 10.0:
             break
@@ -399,21 +629,20 @@ def cpu_baseline(c2, c3):
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "tokens_per_s": round(ntok / t_total, 1), "seconds": round(t_total, 3),
             "runs_s": [round(r, 3) for r in runs], "host_cpu": model, "host_logical_cores": ncpu,
-            "sample": "one full step (decode B=256 on its touched pages + the ragged FP8 prefill call), "
+            "sample": "one full step (decode B=256 on its touched pages + the 16k-token FP8 prefill call), "
                       "single-threaded C oracle in fp64, median of the runs"}
 
 
-def cpu_step(c2, c3):
+def cpu_step(calls):
     import numpy as np
     import oracle
     t_total = 0.0
     nbytes = 0
     ntok = 0
-    for call in (c2, c3):
+    for call in calls:
         inp = call.inp
         if inp.k_cache0 is None:
             # decode pool is 17 GB: run the oracle on the touched pages only
-            import copy
             import torch
             pages = inp.touched_pages()
             pidx = torch.from_numpy(pages).to(call.k_cache.device)
@@ -454,8 +683,17 @@ def copy_calibration(dev):
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
 
 
+# ---------------------------------------------------------------------------
+# the headline run
+# ---------------------------------------------------------------------------
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        if not args.plan:
+            raise SystemExit("--summarize-trace needs --plan")
+        summarize_trace(args.summarize_trace, args.plan)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -474,87 +712,50 @@ def main():
         run_pages_rows(args, dev)
         return
 
-    log("generating decode B=256")
-    c2 = Call(W.c2_decode_b256(), dev)
-    log("generating ragged FP8 prefill")
-    c3 = Call(W.c3_prefill_fp8(), dev)
-    calls = {"decode": c2, "prefill": c3}
-    if args.only == "mla":
-        calls = {"mla": MlaCall(W.c5_mla(), dev)}
-    elif args.only:
-        calls = {args.only: calls[args.only]}
-    names = list(calls)
+    step_names = ["decode", "prefill"]
+    makers = {
+        "decode": lambda: Call(W.c2_decode_b256(), dev),
+        "prefill": lambda: Call(W.c3_prefill_fp8_16k(), dev),
+        "prefill_draw": lambda: Call(W.c3_prefill_fp8(), dev),
+        "mla": lambda: MlaCall(W.c5_mla(), dev),
+    }
+    names = [args.only] if args.only else step_names + ["prefill_draw"]
+    rots = {}
+    for n in names:
+        log(f"generating {n}")
+        rots[n] = Rotation(n, makers[n]())
+        log(f"  {len(rots[n].sets)} sets, {rots[n].touched_bytes / 1e6:.0f} MB touched")
+    step_names = [n for n in step_names if n in rots] or names
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        for c in calls.values():
-            c.launch()
+        for n in step_names:
+            rots[n].launch("step_warmup")
     torch.cuda.synchronize()
-    # the timed region: K whole steps, launches only (an event marker between
-    # launches would itself put a gap of a few microseconds before the next
-    # kernel), bracketed by synchronisations and one event pair
+    # the timed region: K whole steps, launches only, each step on the next
+    # set of every workload, bracketed by synchronisations and one event pair
     log(f"timing {args.steps} steps")
-    e_start = torch.cuda.Event(enable_timing=True)
-    e_stop = torch.cuda.Event(enable_timing=True)
+    e_start, e_stop = _ev(), _ev()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_start.record(stream)
-    for k in range(args.steps):
-        for name in names:
-            calls[name].launch()
+    for _ in range(args.steps):
+        for n in step_names:
+            rots[n].launch("step")
     e_stop.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     ms_events = e_start.elapsed_time(e_stop) / args.steps
-    step_bytes = sum(c.bytes for c in calls.values())
-    step_tokens = sum(c.inp.T for c in calls.values())
+    step_bytes = sum(rots[n].bytes for n in step_names)
+    step_tokens = sum(rots[n].inp.T for n in step_names)
     value = step_bytes / (ms * 1e-3) / 1e9
 
-    # per-kernel duration: HIP events on the launch stream around a run of
-    # back-to-back launches of that kernel (no marker between them)
-    breakdown = {}
-    for name in names:
-        c = calls[name]
-        runs = []
-        for _ in range(3):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(args.kernel_launches):
-                c.launch()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            runs.append(e0.elapsed_time(e1) * 1e3 / args.kernel_launches)
-        avg = sorted(runs)[1]
-        breakdown[name] = {"tokens": c.inp.T, "algorithmic_bytes": c.bytes, "avg_us": round(avg, 2),
-                           "runs_us": [round(r, 2) for r in runs],
-                           "GBps": round(c.bytes / (avg * 1e-6) / 1e9, 1),
-                           "Mtok_per_s": round(c.inp.T / avg, 2)}
-    # the same launches one at a time after a clean flush (512 MiB read)
-    if not args.no_roofline:
-        flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-        for name in names:
-            c = calls[name]
-            durs = []
-            for _ in range(args.roofline_launches):
-                flush.sum()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                c.launch()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                durs.append(e0.elapsed_time(e1) * 1e3)
-            durs.sort()
-            med = percentile(durs, 0.5)
-            breakdown[name]["clean_cache_median_us"] = round(med, 2)
-            breakdown[name]["clean_cache_p10_us"] = round(percentile(durs, 0.1), 2)
-            breakdown[name]["clean_cache_p90_us"] = round(percentile(durs, 0.9), 2)
-            breakdown[name]["clean_cache_GBps"] = round(c.bytes / (med * 1e-6) / 1e9, 1)
-        del flush
-    dominant = max(names, key=lambda n: breakdown[n]["avg_us"])
+    log("per-kernel protocol")
+    flushes = Flushes(dev)
+    breakdown, orders = measure_arms(rots, args, stream, flushes)
+    dominant = max(step_names, key=lambda n: breakdown[n]["rotating_us"])
     log(f"step {ms:.4f} ms, {value:.1f} GB/s; {breakdown}")
 
     b = breakdown[dominant]
@@ -562,14 +763,22 @@ def main():
     traffic = recorded_traffic(khash) if dominant == "prefill" else None
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": b["GBps"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(b["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": b["algorithmic_bytes"], "avg_launch_us": b["avg_us"],
+                "algorithmic_bytes_per_launch": b["algorithmic_bytes"], "avg_launch_us": b["rotating_us"],
+                "mode": f"rotating {b['sets']} sets ({b['rotating_touched_MB']} MB), median of "
+                        f"{args.sessions} sessions x {args.session_launches} back-to-back launches",
+                "same_set_back_to_back_frac": round(b["algorithmic_bytes"] / (b["same_set_back_to_back_us"] * 1e-6)
+                                                    / 1e9 / HBM_PEAK_GBS, 4),
                 "kernel_source_hash": khash}
 
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
         log("timing the CPU oracle on the same step")
-        cpu = cpu_baseline(c2, c3)
+        cpu = cpu_baseline([rots[n].base for n in step_names])
 
+    if args.plan_out:
+        PLAN.dump(args.plan_out)
+
+    prefill_T = rots["prefill"].inp.T if "prefill" in rots else None
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "ms_per_step_events": round(ms_events, 5),
@@ -578,9 +787,9 @@ def main():
         "tokens_per_s": round(step_tokens / (ms * 1e-3), 1),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "config": {"workload": "decode B=256 (32/8/128 bf16, page 16, full pool) + ragged FP8 prefill "
-                               f"(8 req, T={c3.inp.T}, 64/8/128, page 64)",
-                   "step_tokens": step_tokens, "step_algorithmic_bytes": step_bytes, "calls": names},
-        "roofline": roofline, "cpu_baseline": cpu, "breakdown": breakdown,
+                               f"(8 req, T={prefill_T}, 64/8/128, page 64), rotating sets",
+                   "step_tokens": step_tokens, "step_algorithmic_bytes": step_bytes, "calls": step_names},
+        "roofline": roofline, "cpu_baseline": cpu, "breakdown": breakdown, "arm_orders": orders,
     }
     print(json.dumps(out), flush=True)
 

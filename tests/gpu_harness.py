@@ -6,9 +6,10 @@ Tolerances (GPU vs oracle):
 - bit-exact: flags, placement, tail zeros, every byte the call must not
   write, bf16 V copies, the V columns and row padding of an in-place qkv;
 - bf16 Q / K / MLA q_rope / k_pe: <= 2 bf16 ulp on the monotone ordinal
-  line (+0 and -0 equal), or an absolute difference <= 2^-16 (fp32
+  line (+0 and -0 equal); where the oracle's value is below 2^-8 in
+  magnitude, an absolute difference <= 2^-16 is also accepted (fp32
   cancellation in a*c - b*s leaves ~2^-20 absolute error while the bf16
-  ulp vanishes near zero);
+  ulp vanishes near zero; at 2^-8 and above that error is under 1/16 ulp);
 - E4M3 payloads: <= 1 code on the monotone ordinal line;
 - q_scale: relative 1e-5.
 """
@@ -145,6 +146,7 @@ class DeviceNra:
             kv_scale_mode=inp.kv_scale_mode, kv_group_size=inp.kv_group_size,
             k_scale_out=None if self.k_scale_out is None else self.k_scale_out.t,
             v_scale_out=None if self.v_scale_out is None else self.v_scale_out.t,
+            store_policy=inp.store_policy,
         )
 
     def run(self, stream=None):
@@ -240,13 +242,29 @@ def check_bf16(got: np.ndarray, ref: np.ndarray, what: str, stats: dict):
     d = np.abs(bf16_ord(got) - bf16_ord(ref))
     vg = W.bf16_bits_to_f32(got).astype(np.float64)
     vr = W.bf16_bits_to_f32(ref).astype(np.float64)
-    bad = (d > 2) & (np.abs(vg - vr) > 2.0 ** -16)
+    bad = (d > 2) & ~((np.abs(vr) < 2.0 ** -8) & (np.abs(vg - vr) <= 2.0 ** -16))
     stats[what] = {"n": int(got.size), "exact": float((d == 0).mean()) if got.size else 1.0,
                    "max_ulp": int(d.max()) if got.size else 0}
     if bad.any():
         i = np.argwhere(bad)[0]
         raise AssertionError(f"{what}: {int(bad.sum())} bf16 values beyond 2 ulp; first at {tuple(i)}: "
                              f"gpu {vg[tuple(i)]!r} oracle {vr[tuple(i)]!r}")
+
+
+# Shares of values equal to the oracle's that full-size runs must reach: the
+# tolerances above admit a systematic in-tolerance drift (an eps or rsqrt
+# error, a cos/sin row off by one on near-zero outputs); these floors do not.
+EXACT_FLOOR_BF16 = 0.999
+EXACT_FLOOR_E4M3 = 0.99
+
+
+def assert_exact_floors(stats: dict):
+    """Every bf16 / E4M3 comparison in `stats` reached its exact-match floor."""
+    for what, st in stats.items():
+        if "max_ulp" in st and st["n"]:
+            assert st["exact"] >= EXACT_FLOOR_BF16, f"{what}: exact {st['exact']:.6f} < {EXACT_FLOOR_BF16}"
+        if "max_code" in st and st["n"]:
+            assert st["exact"] >= EXACT_FLOOR_E4M3, f"{what}: exact {st['exact']:.6f} < {EXACT_FLOOR_E4M3}"
 
 
 def check_e4m3(got: np.ndarray, ref: np.ndarray, what: str, stats: dict):
@@ -418,7 +436,7 @@ class DeviceMla:
             kv_dtype=qp.FP8_E4M3 if inp.kv_fp8 else qp.BF16, kv_scale=self.kv_scale, q_mode=inp.q_mode,
             q_out=None if self.q_out is None else self.q_out.t,
             q_scale=None if self.q_scale is None else self.q_scale.t, q_scale_inv=self.q_scale_inv,
-            upper_max=inp.upper_max)
+            upper_max=inp.upper_max, store_policy=inp.store_policy)
 
     def run(self, stream=None):
         qp.qkprep_mla_concat_rope_append(stream=stream, **self.kwargs())

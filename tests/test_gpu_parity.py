@@ -37,11 +37,129 @@ def run_and_compare(inp: W.NraInputs) -> dict:
 # the five configurations at full size
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c1", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c1", "c3", "c3_16k", "c4"])
 def test_config_full_size(name):
-    inp = W.CONFIGS[name]()
+    inp = W.c3_prefill_fp8_16k() if name == "c3_16k" else W.CONFIGS[name]()
+    if name == "c3_16k":
+        assert inp.T == 16384 and inp.B == 8 and 1 <= np.diff(inp.q_indptr).min() \
+            and np.diff(inp.q_indptr).max() <= 4096
     stats = run_and_compare(inp)
+    H.assert_exact_floors(stats)
     print(name, inp.T, stats, flush=True)
+
+
+@pytest.mark.parametrize("page_size", [16, 1])
+def test_prefill_16k_small_pages(page_size):
+    """The 16 384-token FP8 prefill at page 16 (1 032 pages) and page 1
+    (16 384 pages): the validation reads and checks every page id the call
+    writes in every workgroup; placement, tails and values as at page 64."""
+    inp = W.c3_prefill_fp8_16k(page_size=page_size, maxp=4096 // page_size)
+    stats = run_and_compare(inp)
+    H.assert_exact_floors(stats)
+    print(page_size, stats, flush=True)
+
+
+_POLICY_CASES = {
+    "prefill_fp8_dyn_padded": lambda: W.c3_prefill_fp8(q_lens=np.array([300, 0, 77, 1025]), name="p"),
+    "decode_bf16": lambda: W.nra_case(seed=71, q_lens=np.ones(40, np.int64),
+                                      prior_lens=np.random.default_rng(71).integers(0, 500, 40),
+                                      Hq=32, Hkv=8, D=128, page_size=16),
+    "d64_static_partial": lambda: W.nra_case(seed=72, q_lens=[33, 70, 5], prior_lens=[0, 12, 90], Hq=8, Hkv=2,
+                                             D=64, page_size=16, kv_fp8=True, k_scale=0.05, v_scale=0.05,
+                                             q_mode=W.Q_FP8_STATIC, q_scale_inv=2.0, rotary_dim=32),
+    "d256_partial_rotary_fp8kv": lambda: W.nra_case(seed=73, q_lens=[40, 9], prior_lens=[3, 100], Hq=4, Hkv=2,
+                                               D=256, page_size=32, kv_fp8=True, k_scale=0.05,
+                                               v_scale=0.05, rotary_dim=96),
+    "redirect_token_scales": lambda: W.nra_case(seed=74, q_lens=[50, 13], prior_lens=[0, 7], Hq=8, Hkv=2,
+                                                D=128, page_size=16, kv_fp8=True, kv_redirect=True,
+                                                kv_scale_mode=W.KV_SCALE_TOKEN, q_mode=W.Q_FP8_DYNAMIC),
+}
+
+
+@pytest.mark.parametrize("case", list(_POLICY_CASES))
+def test_store_policies_write_the_same_bytes(case):
+    """QKPREP_STORE_KEEP (ordinary row stores) and the default streaming
+    stores run different kernel instances; both match the oracle and each
+    other byte for byte."""
+    outs = []
+    for policy in (qp.STORE_STREAM, qp.STORE_KEEP):
+        inp = _POLICY_CASES[case]()
+        inp.store_policy = policy
+        dev = H.DeviceNra(inp)
+        dev.run()
+        torch.cuda.synchronize()
+        assert dev.guards_intact()
+        gpu = dev.host_outputs()
+        H.compare_nra(inp, gpu, H.oracle_outputs(inp))
+        outs.append(gpu)
+    for k in outs[0]:
+        if outs[0][k] is not None:
+            H.check_exact(outs[0][k], outs[1][k], f"{k}: streaming vs keep")
+
+
+@pytest.mark.parametrize("q_mode", [W.Q_BF16, W.Q_FP8_DYNAMIC, W.Q_FP8_STATIC])
+def test_mla_store_policies_write_the_same_bytes(q_mode):
+    outs = []
+    for policy in (qp.STORE_STREAM, qp.STORE_KEEP):
+        inp = W.mla_case(seed=81 + q_mode, T=77, H=24, num_blocks=8, block_size=16, negative_slots=2,
+                         q_mode=q_mode, q_scale_inv=0.5)
+        inp.store_policy = policy
+        dev = H.DeviceMla(inp)
+        dev.run()
+        torch.cuda.synchronize()
+        assert dev.guards_intact()
+        gpu = dev.host_outputs()
+        H.compare_mla(inp, gpu, H.oracle_mla(inp))
+        outs.append(gpu)
+    for k in outs[0]:
+        H.check_exact(outs[0][k], outs[1][k], f"{k}: streaming vs keep")
+
+
+def test_checks_fire_on_planted_corruption():
+    """Negative controls of the checker itself: after a valid call that
+    passes, a guard byte flipped with a plain torch write (no kernel) fails
+    guards_intact(), and a byte flipped in a page the call never writes
+    fails the byte-exact comparison of the untouched cache bytes."""
+    inp = W.nra_case(seed=61, q_lens=[5, 9], prior_lens=[2, 30], Hq=8, Hkv=2, D=128, page_size=16)
+    dev = H.DeviceNra(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    ref = H.oracle_outputs(inp)
+    H.compare_nra(inp, dev.host_outputs(), ref)
+    dev.k_cache.raw[H.GUARD - 1] ^= 0xFF            # the byte just before the cache
+    assert not dev.guards_intact()
+    dev.k_cache.raw[H.GUARD - 1] ^= 0xFF
+    dev.v_cache.raw[-1] ^= 0x01                     # the last guard byte after the V cache
+    assert not dev.guards_intact()
+    dev.v_cache.raw[-1] ^= 0x01
+    assert dev.guards_intact()
+    untouched = np.setdiff1d(np.arange(inp.num_pages), inp.touched_pages())
+    p = int(untouched[len(untouched) // 2])
+    dev.v_cache.t.view(inp.num_pages, -1)[p, 77] ^= 0x0100
+    with pytest.raises(AssertionError, match="v_cache outside appended rows"):
+        H.compare_nra(inp, dev.host_outputs(), ref)
+    dev.v_cache.t.view(inp.num_pages, -1)[p, 77] ^= 0x0100
+    H.compare_nra(inp, dev.host_outputs(), ref)
+
+
+@pytest.mark.parametrize("mutation", ["page_id_negative", "page_id_past_pool"])
+def test_redirect_reads_and_checks_no_page_id(mutation):
+    """With K/V redirected the call writes no page, so page ids are neither
+    read nor checked: an out-of-pool id leaves the call valid, with the
+    oracle's outputs; the other metadata checks still apply (see the
+    malformed-metadata cases)."""
+    q, prior = _ragged(93, B=5, max_q=30, max_prior=100)
+    q[0] = 4
+    inp = W.nra_case(seed=93, q_lens=q, prior_lens=prior, Hq=8, Hkv=2, D=128, page_size=16, kv_fp8=True,
+                     k_scale=0.05, v_scale=0.05, q_mode=W.Q_FP8_DYNAMIC, kv_redirect=True)
+    if mutation == "page_id_negative":
+        inp.page_table[0, (int(inp.seq_lens[0]) - 1) // inp.page_size] = -1
+    else:
+        inp.page_table[2, 0] = inp.num_pages
+    stats = run_and_compare(inp)
+    assert (H.oracle_outputs(inp)["flags"] == 0).all()
+    print(stats, flush=True)
 
 
 def test_c3_with_an_empty_request():
@@ -84,6 +202,7 @@ def test_c2_full_pool():
     cinp = H.compact_inputs(inp, k_before, v_before, pages)
     ref = H.oracle_outputs(cinp)
     stats = H.compare_nra(cinp, gpu, ref)
+    H.assert_exact_floors(stats)
     print(stats, flush=True)
 
 
@@ -94,6 +213,7 @@ def test_c5_mla_full_size():
     torch.cuda.synchronize()
     assert dev.guards_intact()
     stats = H.compare_mla(inp, dev.host_outputs(), H.oracle_mla(inp))
+    H.assert_exact_floors(stats)
     print(stats, flush=True)
 
 
@@ -167,7 +287,9 @@ def test_nope_layer_with_group_kv_scales(D):
 
 def test_nope_layer_full_size_prefill():
     """The 15k-token FP8 prefill of a NoPE layer (rotary_dim = 0)."""
-    print(run_and_compare(W.c3_prefill_fp8(rotary_dim=0)), flush=True)
+    stats = run_and_compare(W.c3_prefill_fp8(rotary_dim=0))
+    H.assert_exact_floors(stats)
+    print(stats, flush=True)
 
 
 @pytest.mark.parametrize("D,R", [(128, 64), (128, 32), (256, 64), (128, 96), (256, 192), (64, 32)])
@@ -175,7 +297,9 @@ def test_partial_rotary_full_size_prefill(D, R):
     """The 15k-token FP8 prefill with partial rotary: round-robin spans, and
     the mirrored loads that read whole lines (all lanes trade up to half the
     head; beyond it only the outer lanes of each row do)."""
-    print(run_and_compare(W.c3_prefill_fp8(D=D, rotary_dim=R)), flush=True)
+    stats = run_and_compare(W.c3_prefill_fp8(D=D, rotary_dim=R))
+    H.assert_exact_floors(stats)
+    print(stats, flush=True)
 
 
 # K/V redirect to caller rows (caches untouched, no tail clear) and dynamic
@@ -593,7 +717,9 @@ def test_mla_fp8_q_full_size(q_mode):
     """The 4096-token, 128-head MLA workload with Q quantised into an E4M3
     q_out: one dynamic scale per token over all heads, or a static scale."""
     inp = W.c5_mla(q_mode=q_mode, q_scale_inv=0.75)
-    print(_run_mla(inp), flush=True)
+    stats = _run_mla(inp)
+    H.assert_exact_floors(stats)
+    print(stats, flush=True)
 
 
 # nope_dim multiple of 32 up to 128 (odd nope-vector counts store 8-byte

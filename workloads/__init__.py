@@ -117,6 +117,8 @@ class NraInputs:
     kv_group_size: int = 0
     k_scale_out0: np.ndarray | None = None   # fp32 [cache rows or T, Hkv, D / group]
     v_scale_out0: np.ndarray | None = None
+    # cache policy of the library's row stores (0 streaming, 1 keep); no effect on values
+    store_policy: int = 0
 
     @property
     def R(self) -> int:
@@ -346,6 +348,7 @@ class MlaInputs:
     upper_max: float = 448.0
     q_out0: np.ndarray | None = None    # uint8 [T, H, nope + rope] (FP8 Q modes)
     q_scale0: np.ndarray | None = None  # fp32 [T] (dynamic)
+    store_policy: int = 0               # cache policy of the library's row stores; no effect on values
 
     @property
     def row_elems(self) -> int:
@@ -444,15 +447,35 @@ def c3_prefill_fp8(seed=1003, empty_request=None, **kw):
     scale in the padded [B, Hq, 4096] layout, upper_max 448,
     k_scale = v_scale = 0.05, tails zeroed, table [40960, 128], theta 1e6."""
     rng = np.random.default_rng(seed)
-    q_lens = rng.integers(1, 4097, size=8)
+    q_lens = np.asarray(kw.pop("q_lens")) if "q_lens" in kw else rng.integers(1, 4097, size=8)
     if empty_request is not None:
         q_lens[empty_request] = 0
-    args = dict(name="c3_prefill_fp8", seed=seed + 7, q_lens=q_lens, prior_lens=np.zeros(8, np.int64),
+    args = dict(name="c3_prefill_fp8", seed=seed + 7, q_lens=q_lens, prior_lens=np.zeros(len(q_lens), np.int64),
                 Hq=64, Hkv=8, D=128, page_size=64, qkv_sigma=2.0, norm=NORM_RMS, theta=1e6,
                 cs_rows=40960, kv_fp8=True, q_mode=Q_FP8_DYNAMIC, q_scale_padded=True,
                 max_seqlen=4096, upper_max=448.0, k_scale=0.05, v_scale=0.05, maxp=64)
     args.update(kw)
     return nra_case(**args)
+
+
+def sixteen_k_lengths(seed=1013, B=8, total=16384, hi=4096):
+    """B request lengths in [1, hi] that sum to exactly `total`: a seeded
+    random composition (B - 1 distinct cut points drawn uniformly from
+    [1, total), redrawn until every part lies in [1, hi])."""
+    rng = np.random.default_rng(seed)
+    while True:
+        cuts = np.sort(rng.choice(np.arange(1, total), size=B - 1, replace=False))
+        lens = np.diff(np.concatenate([[0], cuts, [total]])).astype(np.int64)
+        if lens.min() >= 1 and lens.max() <= hi:
+            return lens
+
+
+def c3_prefill_fp8_16k(seed=1013, **kw):
+    """The ragged FP8 prefill at exactly 16 384 tokens: the C3 shapes and
+    encodings with 8 request lengths in [1, 4096] summing to 16 384."""
+    args = dict(name="c3_prefill_fp8_16k", seed=seed, q_lens=sixteen_k_lengths(seed))
+    args.update(kw)
+    return c3_prefill_fp8(**args)
 
 
 def c4_strided_d256(seed=1004, **kw):
