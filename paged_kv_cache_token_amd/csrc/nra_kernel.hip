@@ -21,9 +21,9 @@
 //  * The sum of squares and the FP8 amax are reduced over the G lanes of the
 //    row only (DPP within the lane group), never across rows or tokens.
 //  * Short calls give every workgroup a balanced, contiguous range of the
-//    (token, chunk) items; long calls deal spans of tokens round-robin, so
-//    the resident workgroups stream through one window of qkv at a time
-//    (grouped by XCD when the padded Q-scale layout is written).  Every
+//    (token, chunk) items; long calls deal short spans of items round-robin,
+//    so the resident workgroups stream through one narrow window of qkv at a
+//    time.  Every
 //    workgroup also owns a range of the requests; the grid is sized to what
 //    stays resident.  Tiles of up to 16 tokens stage their cos/sin rows,
 //    positions and cache row offsets in LDS; the norm weights are staged
@@ -184,7 +184,8 @@ __device__ Verdict validate_requests(const NraDevArgs& a, const int* s_indptr, c
 }
 
 // Validation, step 2: every page id the call writes must lie in the pool.
-// Thread k checks pages k, k + 256, ...; page_id_at() issues one load.
+// Thread k checks pages k, k + 256, ... of the call's flattened page list;
+// page_id_ptr() is the address of page k (the first round's check).
 __device__ __forceinline__ const int* page_id_ptr(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen,
                                                   const int* s_pre, int k) {
     const int b = lds_upper_bound(s_pre, a.B + 1, k) - 1;
@@ -192,14 +193,45 @@ __device__ __forceinline__ const int* page_id_ptr(const NraDevArgs& a, const int
     return a.page_table + (int64_t)b * a.maxp + rp.first + (k - s_pre[b]);
 }
 
-__device__ __forceinline__ int page_id_at(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen,
-                                          const int* s_pre, int k) {
-    return gld(page_id_ptr(a, s_indptr, s_seqlen, s_pre, k));
-}
-
 __device__ __forceinline__ int page_out_of_pool(const NraDevArgs& a, int p) {
     return (p < 0 || p >= a.num_pages) ? 1 : 0;
 }
+
+// Pages k = k0, k0 + 256, ... (< total) of the flattened list: the request
+// of each page is found by walking forward from the request of k0 (one
+// binary search per thread), and the page ids are loaded kPageBatch at a
+// time with independent loads, so a call that writes many pages (a long
+// prefill at a small page size) costs a few memory round trips per
+// workgroup instead of one per 256 pages.  Returns 1 if any id is outside
+// the pool.
+constexpr int kPageBatch = 16;
+
+__device__ int pages_out_of_pool(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen, const int* s_pre,
+                                 int k0, int total) {
+    if (k0 >= total) return 0;
+    int b = lds_upper_bound(s_pre, a.B + 1, k0) - 1;
+    ReqPages rp = request_pages(a, s_indptr, s_seqlen, b);
+    int bad = 0;
+    for (int kb = k0; kb < total; kb += kBlockThreads * kPageBatch) {
+        int v[kPageBatch];
+#pragma unroll
+        for (int u = 0; u < kPageBatch; ++u) {
+            const int k = kb + u * kBlockThreads;
+            const bool in = k < total;
+            // (requests that write no page have s_pre[b] == s_pre[b + 1])
+            while (in && k >= s_pre[b + 1]) {
+                ++b;
+                rp = request_pages(a, s_indptr, s_seqlen, b);
+            }
+            v[u] = gld(in ? a.page_table + (int64_t)b * a.maxp + rp.first + (k - s_pre[b])
+                          : reinterpret_cast<const int*>(g_zero_row));
+        }
+#pragma unroll
+        for (int u = 0; u < kPageBatch; ++u) bad |= page_out_of_pool(a, v[u]);
+    }
+    return bad;
+}
+
 
 template <int D, int QMODE, bool KVFP8>
 struct KvType {
@@ -593,23 +625,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
             return blo < bhi;
         }
         const int64_t span = a.interleave;
-        int64_t tile;
-        if (a.xcd_spans) {
-            // round k covers spans [k grid, k grid + n); the workgroups of
-            // XCD x (blockIdx % 8, the dispatcher's round-robin) take the
-            // contiguous block [n x / 8, n (x + 1) / 8) of them (grid is a
-            // multiple of 8, so every span of a round has a workgroup)
-            const int64_t nsp = (a.total_items + span - 1) / span;
-            const int64_t base = (int64_t)(range_k++) * a.grid;
-            if (base >= nsp) return false;
-            const int64_t n = min((int64_t)a.grid, nsp - base);
-            const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-            const int64_t lo = n * x / 8, hi = n * (x + 1) / 8;
-            if (lo + j >= hi) return false;
-            tile = base + lo + j;
-        } else {
-            tile = blockIdx.x + (int64_t)(range_k++) * a.grid;
-        }
+        const int64_t tile = blockIdx.x + (int64_t)(range_k++) * a.grid;
         if (tile * span >= a.total_items) return false;
         blo = (int)(tile * span);
         bhi = (int)min((int64_t)a.total_items, tile * span + span);
@@ -912,8 +928,8 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
         if (vd.npg >= 1) bad |= page_out_of_pool(a, vd.pg0);
         if (vd.npg >= 2) bad |= page_out_of_pool(a, vd.pg1);
         if (tid < total_pages) bad |= page_out_of_pool(a, p_first);
-        for (int k = tid + kBlockThreads; k < total_pages; k += kBlockThreads)
-            bad |= page_out_of_pool(a, page_id_at(a, s_indptr, s_seqlen, s_pre, k));
+        if (total_pages > kBlockThreads)
+            bad |= pages_out_of_pool(a, s_indptr, s_seqlen, s_pre, tid + kBlockThreads, total_pages);
     }
     bad = block_or4(bad, s_flag);
 
@@ -1063,24 +1079,20 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     if (want < 1) want = 1;
     NraDevArgs la = a;
     la.grid = (int)(want < cap ? want : cap);
-    // Long calls (8 or more tokens per workgroup) deal spans of tokens
-    // round-robin: the resident workgroups then stream through one window of
-    // qkv and the caches instead of the whole call at once, which keeps the
-    // HBM accesses of the moment close together (about 6 % faster on a
-    // 15k-token prefill).  A span is 4 tokens, or about 48 chunks when the
-    // tokens are short (few head rows per token), so that the per-tile
-    // metadata round is spread over enough rows.  Short calls keep one
-    // contiguous range each.
-    const int cpt = a.chunks_per_token;
-    const int span_tok = cpt >= 8 ? 4 : min(kMaxTokensPerTile, (48 + cpt - 1) / cpt);
-    la.interleave = (a.T >= 8 * (int64_t)la.grid) ? span_tok * cpt : 0;
-    // With the padded Q-scale layout a span writes each head's scales as one
-    // 16-byte piece of a 128-byte line that 8 consecutive spans share.  Giving
-    // consecutive spans to workgroups of one XCD lets its L2 merge the pieces
-    // into whole lines (written bytes then equal the algorithmic ones; the
-    // 15k-token prefill gains about 2 us).  Other layouts keep the plain
-    // round-robin, which measured faster for them in steady state.
-    la.xcd_spans = (la.interleave > 0 && a.stage_q_scale && la.grid % 8 == 0) ? 1 : 0;
+    // Long calls (8 or more tokens per workgroup) deal spans of 24 (token,
+    // chunk) items round-robin, not aligned to tokens: the resident
+    // workgroups then stream through one narrow window of qkv and the caches
+    // instead of the whole call at once.  With rotating buffers (the previous
+    // calls' outputs still being written back) 24-item spans measured best
+    // or near best on every prefill shape: the 15k-token FP8 prefill 96.4 ->
+    // 88.5 us against 4-token spans (40 items), the 16k one 103.6 -> 95.8,
+    // 64-dim heads 52.5 -> 51.4, the strided 256-dim one 50.8 -> 49.3; 20 to
+    // 32 items are close, 12 or 16 items slower (the per-tile metadata round
+    // then dominates), 48 slower.  Grouping a round's spans by XCD (so that
+    // one L2 merges the padded Q scales into whole lines) measured 5 us slower
+    // in that mode and is not done.  Short calls keep one contiguous range
+    // each.
+    la.interleave = (a.T >= 8 * (int64_t)la.grid) ? 24 : 0;
     (void)hipGetLastError();   // the status below then covers this launch only
     hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, ROT, MEM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();

@@ -100,7 +100,6 @@ struct NraDevArgs {
     float* v_scale_out;
     int32_t mem;                        // kMemInPlace / kMemStream / kMemKeep
     int32_t interleave;                 // items per round-robin span, 0 = one range per workgroup
-    int32_t xcd_spans;                  // spans of a round grouped by XCD (blockIdx % 8)
     int32_t grid;                       // workgroups launched (set by the launcher)
 };
 
