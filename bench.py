@@ -23,11 +23,11 @@ launches' dirty output lines are written back to HBM while it runs: the
 steady state of a serving loop.  The timed steps rotate the same way.
 
 Per-kernel timing (the roofline): 20 warm-up launches of each kernel, then
-3 sessions of 200 launches, each session timing a back-to-back run of
-rotating launches of each kernel with one HIP event pair on the launch
-stream (no marker between launches: on this GPU an event marker delays the
-next kernel by several microseconds); the kernel order alternates between
-sessions.  Also reported, as extra keys: the same kernel back-to-back on one
+3 sessions; in each, every kernel gets 20 more untimed launches and then a
+timed back-to-back run of 200 rotating launches with one HIP event pair on
+the launch stream (no marker between launches: on this GPU an event marker
+delays the next kernel by several microseconds); the kernel order
+alternates between sessions.  Also reported, as extra keys: the same kernel back-to-back on one
 set (its previous outputs still in the Infinity Cache), and single launches
 after a 512 MiB read flush or a 512 MiB write flush (events around each
 launch, so those figures include the launch latency).
@@ -75,8 +75,11 @@ def parse(argv=None):
     ap.add_argument("--flush-launches", type=int, default=50,
                     help="single launches after a read flush and after a write flush (extra keys)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "prefill_draw", "mla"], default=None,
-                    help="time one workload alone (counter runs)")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated workloads (decode, prefill, prefill_draw, mla or any suite workload), "
+                         "each timed alone with a short rotating run: counter runs")
+    ap.add_argument("--counted-launches", type=int, default=10,
+                    help="rotating launches per workload after 5 warm-ups with --only")
     ap.add_argument("--plan-out", default=None,
                     help="write the ordered list of library launches (workload, phase, count) as JSON")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -91,6 +94,9 @@ def parse(argv=None):
     ap.add_argument("--summarize-trace", default=None,
                     help="rocprofv3 kernel_trace.csv to summarise per phase (needs --plan); no GPU")
     ap.add_argument("--plan", default=None, help="launch plan written by --plan-out")
+    ap.add_argument("--summarize-counters", default=None,
+                    help="rocprofv3 --pmc counter_collection.csv to summarise per workload (needs --plan); no GPU")
+    ap.add_argument("--phase", default="counted", help="plan phase whose launches --summarize-counters averages")
     return ap.parse_args(argv)
 
 
@@ -182,6 +188,41 @@ def summarize_trace(csv_path, plan_path):
         kname = kname.split("(")[0]
         print(f"| {wl} | {phase} | {len(v)} | {sum(v) / len(v):.2f} | {percentile(v, 0.5):.2f} | "
               f"{percentile(v, 0.1):.2f} | {percentile(v, 0.9):.2f} | `{kname}` |")
+
+
+def summarize_counters(csv_path, plan_path, phase):
+    """Mean of every counter per library launch of each workload in a
+    rocprofv3 --pmc run, over the plan's launches of `phase`, matched in
+    dispatch order.  Prints one line per (workload, counter) as JSON."""
+    import csv
+    with open(plan_path) as f:
+        runs = json.load(f)["runs"]
+    disp = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name", "")
+            if not ("nra_kernel" in name or "mla_kernel" in name or "mla_q8_kernel" in name):
+                continue
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"kernel": name, "c": {}})
+            c = r["Counter_Name"]
+            d["c"][c] = d["c"].get(c, 0.0) + float(r["Counter_Value"])
+    order = [disp[k] for k in sorted(disp)]
+    want = sum(n for _, _, n in runs)
+    if len(order) != want:
+        raise SystemExit(f"counter file holds {len(order)} library launches, the plan {want}")
+    out = {}
+    k = 0
+    for wl, ph, n in runs:
+        if ph == phase:
+            acc = out.setdefault(wl, {"launches": 0, "sum": {}})
+            for d in order[k:k + n]:
+                acc["launches"] += 1
+                for c, v in d["c"].items():
+                    acc["sum"][c] = acc["sum"].get(c, 0.0) + v
+        k += n
+    for wl, acc in out.items():
+        mean = {c: v / acc["launches"] for c, v in acc["sum"].items()}
+        print(json.dumps({"workload": wl, "launches": acc["launches"], "mean_per_launch": mean}))
 
 
 # ---------------------------------------------------------------------------
@@ -454,6 +495,11 @@ def measure_arms(rots, args, stream, flushes):
         orders.append(list(order))
         for n in order:
             r = rots[n]
+            # 20 more untimed launches right before each timed run: a kernel
+            # that follows a light one (the decode) otherwise runs its first
+            # milliseconds on a memory system not yet at full speed
+            for _ in range(20):
+                r.launch(f"warmup_s{s + 1}")
             sess[n].append(time_run(lambda: r.launch(f"rotating_s{s + 1}"), args.session_launches, stream))
     res = {}
     for n in names:
@@ -687,12 +733,50 @@ def copy_calibration(dev):
 # the headline run
 # ---------------------------------------------------------------------------
 
+def run_only(args, dev, makers):
+    """Each named workload alone: 5 warm-up launches, then
+    --counted-launches rotating launches (one event pair around them): the
+    short runs that rocprofv3 counter passes profile."""
+    import torch
+    stream = torch.cuda.current_stream()
+    suite = suite_workloads()
+    table = {}
+    for name in [n for n in args.only.split(",") if n]:
+        if name in makers:
+            base = makers[name]()
+        elif name in suite:
+            make, kind = suite[name]
+            inp = make()
+            base = MlaCall(inp, dev) if kind == "mla" else Call(inp, dev)
+        else:
+            raise SystemExit(f"unknown workload {name}")
+        rot = Rotation(name, base)
+        log(f"{name}: {len(rot.sets)} sets")
+        for _ in range(5):
+            rot.launch("warmup")
+        torch.cuda.synchronize()
+        us = time_run(lambda: rot.launch("counted"), args.counted_launches, stream)
+        table[name] = {"tokens": rot.inp.T, "algorithmic_bytes": rot.bytes, "sets": len(rot.sets),
+                       "rotating_us": round(us, 2), "launches": args.counted_launches}
+        log(f"  {table[name]}")
+        del rot, base
+        torch.cuda.empty_cache()
+    if args.plan_out:
+        PLAN.dump(args.plan_out)
+    print(json.dumps({"only": table}), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
         if not args.plan:
             raise SystemExit("--summarize-trace needs --plan")
         summarize_trace(args.summarize_trace, args.plan)
+        return
+    if args.summarize_counters:
+        if not args.plan:
+            raise SystemExit("--summarize-counters needs --plan")
+        summarize_counters(args.summarize_counters, args.plan, args.phase)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
@@ -719,13 +803,15 @@ def main():
         "prefill_draw": lambda: Call(W.c3_prefill_fp8(), dev),
         "mla": lambda: MlaCall(W.c5_mla(), dev),
     }
-    names = [args.only] if args.only else step_names + ["prefill_draw"]
+    if args.only:
+        run_only(args, dev, makers)
+        return
+    names = step_names + ["prefill_draw"]
     rots = {}
     for n in names:
         log(f"generating {n}")
         rots[n] = Rotation(n, makers[n]())
         log(f"  {len(rots[n].sets)} sets, {rots[n].touched_bytes / 1e6:.0f} MB touched")
-    step_names = [n for n in step_names if n in rots] or names
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -771,7 +857,7 @@ def main():
                 "kernel_source_hash": khash}
 
     cpu = None
-    if not args.no_cpu_baseline and args.only is None:
+    if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same step")
         cpu = cpu_baseline([rots[n].base for n in step_names])
 

@@ -287,8 +287,10 @@ typedef struct qkprep_mla_params {
     const float* q_scale_inv;      /* FP8_STATIC: device fp32 scalar */
     float upper_max;               /* FP8_DYNAMIC: finite, in (0, 448] */
 
-    int32_t store_policy;          /* qkprep_store_policy (0 = QKPREP_STORE_STREAM; the in-place
-                                      q rope slices follow it too) */
+    int32_t store_policy;          /* qkprep_store_policy (0 = QKPREP_STORE_STREAM); the latent rows
+                                      and the in-place q rope slices follow it; the E4M3 q_out rows
+                                      always take ordinary stores (written in 64-byte pieces that L2
+                                      merges into whole lines) */
 } qkprep_mla_params;
 
 /* Host checks, then one kernel launch on `stream` (none when there is no
