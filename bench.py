@@ -84,6 +84,12 @@ def parse(argv=None):
                     help="write the ordered list of library launches (workload, phase, count) as JSON")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB copy (counter calibration) and exit")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="time the smallest kernels (a 1-workgroup and a 256-workgroup fill) back to back and "
+                         "after a cache flush, as the floor under latency-bound calls; then exit")
+    ap.add_argument("--stream-calibration", action="store_true",
+                    help="time plain torch streams (2 reads : 1 write, copy, read-only) with the prefill's "
+                         "bytes in the same rotating protocol, as a reference for the roofline; then exit")
     ap.add_argument("--suite", action="store_true",
                     help="time every workload (the five configurations and the variant rows) one by one "
                          "and print one JSON object; no headline line")
@@ -137,12 +143,30 @@ class Plan:
 
     def __init__(self):
         self.runs = []
+        self.captured = None
 
     def add(self, name, phase, n=1):
+        if self.captured is not None:
+            # launches recorded into a graph run on the GPU at its replays
+            self.captured.append(name)
+            return
+        if n <= 0:
+            return
         if self.runs and self.runs[-1][0] == name and self.runs[-1][1] == phase:
             self.runs[-1][2] += n
         else:
             self.runs.append([name, phase, n])
+
+    def begin_capture(self):
+        self.captured = []
+
+    def end_capture(self):
+        names, self.captured = self.captured, None
+        return names
+
+    def replay(self, names, phase):
+        for n in names:
+            self.add(n, phase)
 
     def dump(self, path):
         with open(path, "w") as f:
@@ -422,6 +446,10 @@ class Rotation:
     def launch_same(self, phase):
         self.sets[0].launch()
         PLAN.add(self.name, phase)
+
+    def set_stream(self, handle):
+        for c in self.sets:
+            c._stream = handle
 
 
 # ---------------------------------------------------------------------------
@@ -729,6 +757,83 @@ def copy_calibration(dev):
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
 
 
+def launch_floor(args, dev):
+    """Durations of the smallest kernels on this GPU in the protocols used
+    for the calls: torch fills of 64 floats (one workgroup) and of 65 536
+    floats (256 workgroups of 256 threads, the decode's grid), 200 launches
+    back to back with one event pair (kernel time + dispatch gap), and
+    single launches after a 512 MiB write flush with events around each
+    (including the launch latency)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    flushes = Flushes(dev)
+    out = {}
+    for name, n in (("fill_1_workgroup", 64), ("fill_256_workgroups", 256 * 256)):
+        x = torch.empty(n, device=dev, dtype=torch.float32)
+        fn = lambda: x.fill_(1.0)  # noqa: E731
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        b2b = sorted(time_run(fn, 200, stream) for _ in range(args.sessions))
+        wf = time_single(fn, 100, flushes.write, stream)
+        out[name] = {"back_to_back_us": round(b2b[len(b2b) // 2], 2),
+                     "write_flush_median_us": round(percentile(wf, 0.5), 2)}
+        log(f"{name}: {out[name]}")
+    print(json.dumps({"launch_floor": out}), flush=True)
+
+
+def stream_calibration(args, dev):
+    """Plain library streams moving the 16k-token prefill's bytes (reads
+    343.9 MB, writes 172.4 MB) in the roofline protocol (rotating sets, 20
+    warm-ups, sessions of back-to-back launches with one event pair): an
+    elementwise bf16 add c = a + b (2 reads : 1 write, the prefill's mix), a
+    copy (1 : 1) and a sum (read only).  torch's kernels use ordinary loads
+    and stores.  A reference for what the memory system gives a simple
+    kernel in this protocol, not a bound."""
+    import torch
+    stream = torch.cuda.current_stream()
+    wr = 172_392_448                              # the prefill's written bytes
+    n = wr // 2                                   # bf16 elements per operand
+    S = 4
+    sets = [(torch.randn(n, device=dev, dtype=torch.bfloat16), torch.randn(n, device=dev, dtype=torch.bfloat16),
+             torch.empty(n, device=dev, dtype=torch.bfloat16)) for _ in range(S)]
+    k = {"i": 0}
+
+    def nxt():
+        k["i"] = (k["i"] + 1) % S
+        return sets[k["i"]]
+
+    def add():
+        a, b, c = nxt()
+        torch.add(a, b, out=c)
+
+    def copy():
+        a, _, c = nxt()
+        c.copy_(a)
+
+    def rsum():
+        a, b, _ = nxt()
+        torch.sum(a)
+    arms = {"add_2r1w": (add, 2 * n * 2 + n * 2), "copy_1r1w": (copy, 2 * n * 2), "sum_read": (rsum, n * 2)}
+    out = {}
+    for name, (fn, nbytes) in arms.items():
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        sess = []
+        for _ in range(args.sessions):
+            for _ in range(20):
+                fn()
+            sess.append(time_run(fn, args.session_launches, stream))
+        med = sorted(sess)[len(sess) // 2]
+        out[name] = {"bytes": nbytes, "us": round(med, 2), "session_us": [round(x, 2) for x in sess],
+                     "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                     "pct_of_peak": round(100 * nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+        log(f"{name}: {out[name]}")
+    print(json.dumps({"stream_calibration": out, "sets": S, "note": "torch kernels, ordinary loads/stores"}),
+          flush=True)
+
+
 # ---------------------------------------------------------------------------
 # the headline run
 # ---------------------------------------------------------------------------
@@ -789,6 +894,12 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev)
         return
+    if args.stream_calibration:
+        stream_calibration(args, dev)
+        return
+    if args.launch_floor:
+        launch_floor(args, dev)
+        return
     if args.suite:
         run_suite(args, dev)
         return
@@ -819,21 +930,50 @@ def main():
         for n in step_names:
             rots[n].launch("step_warmup")
     torch.cuda.synchronize()
-    # the timed region: K whole steps, launches only, each step on the next
-    # set of every workload, bracketed by synchronisations and one event pair
+    # The K steps are captured once as one HIP graph (each step on the next
+    # set of every workload, as eager launches would take them) and the timed
+    # region replays it: K whole steps with no host launch cost in between,
+    # bracketed by synchronisations and one event pair.  The same K steps
+    # launched eagerly from Python are timed after it as an extra key: on
+    # some hosts two launches per step cannot keep the GPU busy.
+    log(f"capturing {args.steps} steps as a graph")
+    cap = torch.cuda.Stream()
+    for n in step_names:
+        rots[n].set_stream(cap.cuda_stream)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    PLAN.begin_capture()
+    with torch.cuda.graph(graph, stream=cap):
+        for _ in range(args.steps):
+            for n in step_names:
+                rots[n].launch("step")
+    captured = PLAN.end_capture()
+    for n in step_names:
+        rots[n].set_stream(stream.cuda_stream)
+    for _ in range(2):
+        graph.replay()           # untimed replays: the graph's first launch uploads it
+        PLAN.replay(captured, "step_warmup_replay")
+    torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     e_start, e_stop = _ev(), _ev()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_start.record(stream)
-    for _ in range(args.steps):
-        for n in step_names:
-            rots[n].launch("step")
+    graph.replay()
     e_stop.record(stream)
+    PLAN.replay(captured, "step")
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     ms_events = e_start.elapsed_time(e_stop) / args.steps
+    # the same steps launched eagerly (extra key)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        for n in step_names:
+            rots[n].launch("step_eager")
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t2) * 1e3 / args.steps
     step_bytes = sum(rots[n].bytes for n in step_names)
     step_tokens = sum(rots[n].inp.T for n in step_names)
     value = step_bytes / (ms * 1e-3) / 1e9
@@ -868,6 +1008,8 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "ms_per_step_events": round(ms_events, 5),
+        "timed_as": f"one HIP graph replay of the {args.steps} steps",
+        "ms_per_step_eager_launches": round(ms_eager, 5),
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "tokens_per_s": round(step_tokens / (ms * 1e-3), 1),
