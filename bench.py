@@ -609,6 +609,8 @@ def run_suite(args, dev):
         log(f"  {table[name]}")
         del rot, base
         torch.cuda.empty_cache()
+    if args.plan_out:
+        PLAN.dump(args.plan_out)
     print(json.dumps({"suite": table, "peak_GBps": HBM_PEAK_GBS, "sessions": args.sessions,
                       "session_launches": args.session_launches}), flush=True)
 
@@ -636,6 +638,8 @@ def run_pages_rows(args, dev):
         log(f"  {r}")
         del rot
         torch.cuda.empty_cache()
+    if args.plan_out:
+        PLAN.dump(args.plan_out)
     print(json.dumps({"pages_rows": table}), flush=True)
 
 
