@@ -85,7 +85,7 @@ def parse(argv=None):
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 256 MiB copy (counter calibration) and exit")
     ap.add_argument("--launch-floor", action="store_true",
-                    help="time the smallest kernels (a 1-workgroup and a 256-workgroup fill) back to back and "
+                    help="time the smallest kernels (a 1-workgroup and a 64-workgroup fill) back to back and "
                          "after a cache flush, as the floor under latency-bound calls; then exit")
     ap.add_argument("--stream-calibration", action="store_true",
                     help="time plain torch streams (2 reads : 1 write, copy, read-only) with the prefill's "
@@ -95,7 +95,7 @@ def parse(argv=None):
                          "and print one JSON object; no headline line")
     ap.add_argument("--suite-only", default=None, help="comma-separated subset of the suite's workloads")
     ap.add_argument("--pages-rows", action="store_true",
-                    help="time the FlashInfer PR's measured rows, rebuilt, after a cache flush each, and "
+                    help="time the FlashInfer PR's measured rows, rebuilt, in the rotating protocol, and "
                          "print them beside that PR's B200 / H100 latencies (context only)")
     ap.add_argument("--summarize-trace", default=None,
                     help="rocprofv3 kernel_trace.csv to summarise per phase (needs --plan); no GPU")
@@ -764,7 +764,7 @@ def copy_calibration(dev):
 def launch_floor(args, dev):
     """Durations of the smallest kernels on this GPU in the protocols used
     for the calls: torch fills of 64 floats (one workgroup) and of 65 536
-    floats (256 workgroups of 256 threads, the decode's grid), 200 launches
+    floats (64 workgroups of 256 threads, 4 floats per thread), 200 launches
     back to back with one event pair (kernel time + dispatch gap), and
     single launches after a 512 MiB write flush with events around each
     (including the launch latency)."""
@@ -772,7 +772,7 @@ def launch_floor(args, dev):
     stream = torch.cuda.current_stream()
     flushes = Flushes(dev)
     out = {}
-    for name, n in (("fill_1_workgroup", 64), ("fill_256_workgroups", 256 * 256)):
+    for name, n in (("fill_1_workgroup", 64), ("fill_64_workgroups", 256 * 256)):
         x = torch.empty(n, device=dev, dtype=torch.float32)
         fn = lambda: x.fill_(1.0)  # noqa: E731
         for _ in range(20):
@@ -999,6 +999,11 @@ def main():
                 "same_set_back_to_back_frac": round(b["algorithmic_bytes"] / (b["same_set_back_to_back_us"] * 1e-6)
                                                     / 1e9 / HBM_PEAK_GBS, 4),
                 "kernel_source_hash": khash}
+    if traffic is not None:
+        roofline["traffic_source"] = ("L2-side FETCH_SIZE (x 1.99978) + WRITE_SIZE (x 1.0) per launch from "
+                                      "profiles/nra_prefill_fp8_16k_counters.txt: an upper bound on HBM "
+                                      "traffic (the Infinity Cache sits below the L2)")
+        roofline["traffic_ratio"] = round(traffic / b["algorithmic_bytes"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
