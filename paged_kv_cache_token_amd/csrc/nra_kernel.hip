@@ -105,10 +105,13 @@ __device__ __forceinline__ ReqPages request_pages(const NraDevArgs& a, const int
 // Validation, step 1: per-request checks and, on the full path, the
 // block-wide exclusive prefix s_pre[0..B] of the number of pages each
 // request writes, with the request and page-table column of each of the
-// first kPageSlots pages (s_pgreq / s_pgcol).  Needs s_indptr / s_seqlen
-// staged.  Returns this thread's partial verdict and the path taken.
+// first kPageSlots pages (s_pgreq / s_pgcol).  With the page ids read as
+// 16-byte vectors (a.pt_vec, at most kSearchRequests requests) it also writes
+// s_vpre[0..B], the prefix of the number of whole vectors inside each
+// request's written columns.  Needs s_indptr / s_seqlen staged.  Returns this thread's
+// partial verdict and the path taken.
 constexpr int kPageSlots = kBlockThreads;   // pages located by table lookup (one per thread)
-constexpr int kSearchRequests = 64;         // up to this many requests, pages are found by binary search
+static_assert(kSearchRequests <= 64, "the vector prefix is one wave's scan");
 
 // The same pass also writes the request of each of the first tile's tokens
 // (s_treq[t - t_first] for t in [t_first, t_first + ntok)), since it visits
@@ -129,15 +132,15 @@ struct Verdict {
 };
 
 __device__ Verdict validate_requests(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen, int* s_pre,
-                                     int* s_wave, int* s_vote, int* s_pgreq, int* s_pgcol, int* s_treq,
-                                     int t_first, int ntok) {
+                                     int* s_wave, int* s_vote, int* s_pgreq, int* s_pgcol, int* s_vpre,
+                                     int* s_treq, int t_first, int ntok) {
     const int tid = threadIdx.x;
     const int B = a.B;
     int bad = 0;
     if (tid == 0 && (s_indptr[0] != 0 || s_indptr[B] != a.T)) bad = 1;
     const int per = (B + kBlockThreads - 1) / kBlockThreads;
     const int lo = min(B, tid * per), hi = min(B, lo + per);
-    int sum = 0, few = 1;
+    int sum = 0, few = 1, vsum = 0;
     ReqPages rp_lo{0, 0, 0};   // request lo's pages, kept for the second pass
     for (int b = lo; b < hi; ++b) {
         const int t0 = max(s_indptr[b], t_first), t1 = min(s_indptr[b + 1], t_first + ntok);
@@ -147,6 +150,8 @@ __device__ Verdict validate_requests(const NraDevArgs& a, const int* s_indptr, c
         bad |= rp.bad;
         sum += rp.count;
         few &= rp.count <= kFastPages ? 1 : 0;
+        // whole 16-byte vectors of the page-table row inside columns [first, first + count)
+        if (rp.count > 0) vsum += max(((rp.first + rp.count) >> 2) - ((rp.first + 3) >> 2), 0);
     }
     // the own request's page ids (a valid request's pages lie inside its
     // page-table row; an invalid one has count 0 and reads the zero row)
@@ -179,6 +184,12 @@ __device__ Verdict validate_requests(const NraDevArgs& a, const int* s_indptr, c
         run += rp.count;
     }
     if (tid == kBlockThreads - 1) s_pre[B] = base + incl;
+    if (a.pt_vec) {
+        // B <= kSearchRequests <= 64: every request is owned by a lane of wave 0
+        const int vincl = wave_inclusive_scan(vsum);
+        if (wave == 0 && lo < hi) s_vpre[lo] = vincl - vsum;
+        if (tid == B - 1) s_vpre[B] = vincl;
+    }
     __syncthreads();
     return Verdict{bad, 0, 0, 0, 0};
 }
@@ -230,6 +241,75 @@ __device__ int pages_out_of_pool(const NraDevArgs& a, const int* s_indptr, const
         for (int u = 0; u < kPageBatch; ++u) bad |= page_out_of_pool(a, v[u]);
     }
     return bad;
+}
+
+
+// Every page id the call writes, with the page table read as 16-byte
+// vectors (a.pt_vec: the table and its rows are 16-byte aligned).  Each
+// request's written columns [first, first + count) split into whole vectors
+// and at most 3 + 3 columns at the two ends.  The whole vectors of all
+// requests are numbered consecutively (prefix s_vpre); thread k takes
+// vectors k, k + 256, ..., kVecBatch of them in flight, walking forward over
+// the requests as the pages walk does, and keeps the unsigned maximum of the
+// ids (a negative id compares above the pool as well).  Thread b < B reads
+// the end columns of request b one by one, in the same round as its first
+// vectors.  Returns 1 if any id is outside the pool.
+constexpr int kVecBatch = 4;
+
+__device__ __forceinline__ int first_whole_vector(int first) { return (first + 3) >> 2; }
+
+__device__ int page_vectors_out_of_pool(const NraDevArgs& a, const int* s_indptr, const int* s_seqlen,
+                                        const int* s_vpre) {
+    const int tid = threadIdx.x;
+    const int* zi = reinterpret_cast<const int*>(g_zero_row);
+    // the end columns of request tid, outside its whole vectors (a column
+    // not written reads the zero row, which is inside the pool)
+    uint32_t e[6];
+    {
+        const int b = min(tid, a.B - 1);
+        const ReqPages rp = request_pages(a, s_indptr, s_seqlen, b);
+        const bool own = tid < a.B && rp.count > 0;
+        const int lo = rp.first, hi = rp.first + rp.count;
+        const int head_end = min(hi, 4 * first_whole_vector(lo));   // [lo, head_end)
+        const int tail_beg = max(lo, 4 * (hi >> 2));                // [tail_beg, hi)
+        const int* rowp = a.page_table + (int64_t)b * a.maxp;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            e[j] = (uint32_t)gld(own && lo + j < head_end ? rowp + lo + j : zi);
+            e[3 + j] = (uint32_t)gld(own && tail_beg + j < hi ? rowp + tail_beg + j : zi);
+        }
+    }
+    // the whole vectors
+    uint32_t mx = 0;
+    const int total = s_vpre[a.B];
+    if (tid < total) {
+        int b = lds_upper_bound(s_vpre, a.B + 1, tid) - 1;
+        int v_lo = s_vpre[b], v_hi = s_vpre[b + 1];
+        const u32x4_t* row = reinterpret_cast<const u32x4_t*>(a.page_table + (int64_t)b * a.maxp) +
+                             first_whole_vector(request_pages(a, s_indptr, s_seqlen, b).first);
+        for (int kb = tid; kb < total; kb += kBlockThreads * kVecBatch) {
+            u32x4_t v[kVecBatch];
+#pragma unroll
+            for (int u = 0; u < kVecBatch; ++u) {
+                const int k = kb + u * kBlockThreads;
+                const bool in = k < total;
+                // (requests with no whole vector have s_vpre[b] == s_vpre[b + 1])
+                while (in && k >= v_hi) {
+                    ++b;
+                    v_lo = v_hi;
+                    v_hi = s_vpre[b + 1];
+                    row = reinterpret_cast<const u32x4_t*>(a.page_table + (int64_t)b * a.maxp) +
+                          first_whole_vector(request_pages(a, s_indptr, s_seqlen, b).first);
+                }
+                v[u] = gld(in ? row + (k - v_lo) : reinterpret_cast<const u32x4_t*>(g_zero_row));
+            }
+#pragma unroll
+            for (int u = 0; u < kVecBatch; ++u) mx = max(max(mx, max(v[u].x, v[u].y)), max(v[u].z, v[u].w));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 6; ++j) mx = max(mx, e[j]);
+    return mx >= (uint32_t)a.num_pages ? 1 : 0;
 }
 
 
@@ -571,10 +651,22 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     __shared__ int s_tail[kTailPrefetch];
     __shared__ int s_pgreq[kPageSlots];              // request of page slot k
     __shared__ int s_pgcol[kPageSlots];              // its page-table column
+    __shared__ int s_vpre[kSearchRequests + 1];      // page-id vectors before request b (a.pt_vec)
     __shared__ int s_treq[kMaxTokensPerTile];        // request of each tile token
     __shared__ int s_flag[4];
 
-    preload_kernargs(a);
+    {
+        // One scalar load per 32 bytes of the arguments at entry brings every
+        // line of the struct into the scalar cache in one burst (on a fresh
+        // launch the kernarg loads miss), and the later loads of the other
+        // fields hit there.  Forcing all ~90 dwords into SGPRs instead kept
+        // them live: the allocator then spilled ~180 SGPRs into VGPR lanes,
+        // and the readlanes cost 0.2-0.6 us per decode and ~1 % of a long
+        // prefill.
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&a);
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(NraDevArgs) / 4); i += 8) asm volatile("" ::"s"(w[i]));
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: cursor math stays scalar
@@ -904,8 +996,8 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     if (a.paged) {
         // (the first tile's token -> request map is written in the same
         // pass; the barriers inside make it visible)
-        vd = validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave, s_vote, s_pgreq, s_pgcol, s_treq, t_first,
-                               have_items ? ntok : 0);
+        vd = validate_requests(a, s_indptr, s_seqlen, s_pre, s_wave, s_vote, s_pgreq, s_pgcol, s_vpre, s_treq,
+                               t_first, have_items ? ntok : 0);
         bad = vd.bad;
     }
     {
@@ -915,21 +1007,29 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
         // page counts of an inconsistent request are zero and the row lookups
         // are clamped); nothing is written unless the whole call is valid.
         const int total_pages = (a.paged && !vd.fast) ? s_pre[a.B] : 0;
+        // Calls that write more pages than threads read the ids in a second
+        // round anyway; there the vector walk below checks every page.  Up to
+        // kBlockThreads pages, one id per thread in this round is cheaper.
+        const bool vec = a.pt_vec && total_pages > kBlockThreads;
         const int ks = min(tid, max(min(total_pages, kPageSlots) - 1, 0));
         const int* pp = reinterpret_cast<const int*>(g_zero_row);
-        if (total_pages > 0)
+        if (total_pages > 0 && !vec)
             pp = a.B > kSearchRequests ? a.page_table + (int64_t)s_pgreq[ks] * a.maxp + s_pgcol[ks]
                                        : page_id_ptr(a, s_indptr, s_seqlen, s_pre, ks);
         const int p_first = gld(pp);
         const RowsFetch rf = fetch_rows();
         const int tail_page = fetch_tail();
+        // (the vector walk's first loads go out while the lookups above are in flight)
+        if (vec) bad |= page_vectors_out_of_pool(a, s_indptr, s_seqlen, s_vpre);
         if (have_items) store_rows(rf);
         if (a.paged) store_tail(tail_page);
         if (vd.npg >= 1) bad |= page_out_of_pool(a, vd.pg0);
         if (vd.npg >= 2) bad |= page_out_of_pool(a, vd.pg1);
-        if (tid < total_pages) bad |= page_out_of_pool(a, p_first);
-        if (total_pages > kBlockThreads)
-            bad |= pages_out_of_pool(a, s_indptr, s_seqlen, s_pre, tid + kBlockThreads, total_pages);
+        if (!vec) {
+            if (tid < total_pages) bad |= page_out_of_pool(a, p_first);
+            if (total_pages > kBlockThreads)
+                bad |= pages_out_of_pool(a, s_indptr, s_seqlen, s_pre, tid + kBlockThreads, total_pages);
+        }
     }
     bad = block_or4(bad, s_flag);
 

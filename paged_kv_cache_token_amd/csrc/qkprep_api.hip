@@ -186,6 +186,10 @@ qkprep_status qkprep_norm_rope_append(const qkprep_norm_rope_append_params* p, h
     a.B = B;
     a.q_indptr = p->q_indptr; a.seq_lens = p->seq_lens; a.page_table = p->page_table;
     a.maxp = p->max_pages_per_request;
+    a.pt_vec = paged && !redirect && B <= kSearchRequests && aligned16(p->page_table) &&
+                       p->max_pages_per_request % 4 == 0
+                   ? 1
+                   : 0;
     a.slot_mapping = p->slot_mapping;
     a.k_cache = redirect ? p->out_k : p->k_cache;
     a.v_cache = redirect ? p->out_v : p->v_cache;

@@ -106,7 +106,9 @@ __device__ __forceinline__ float4 ldf4(const float* p) {
 // compiler otherwise loads each field from the kernarg segment where it is
 // first used, and on a fresh launch each of those scalar loads misses: a
 // kernel whose phases use different fields pays one memory round trip per
-// phase.  Forcing all fields into SGPRs at entry turns that into one burst.
+// phase.  Forcing all fields into SGPRs at entry turns that into one burst
+// (for structs small enough to stay in SGPRs; the norm-rope-append kernel
+// touches one dword per 32 bytes instead).
 template <typename T>
 __device__ __forceinline__ void preload_kernargs(const T& args) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(&args);

@@ -19,6 +19,9 @@ constexpr int kMaxStagedQHeads = 256;
 constexpr int kBatch = 2;
 // tail pages of the first requests a workgroup clears, prefetched with the metadata
 constexpr int kTailPrefetch = 16;
+// up to this many requests the validation finds a page's request by binary
+// search, and reads the page ids as 16-byte vectors when the table allows it
+constexpr int kSearchRequests = 64;
 
 // Division of a non-negative 31-bit integer by a runtime divisor d >= 1
 // without a division instruction (Granlund and Montgomery, "Division by
@@ -99,6 +102,8 @@ struct NraDevArgs {
     float* k_scale_out;
     float* v_scale_out;
     int32_t mem;                        // kMemInPlace / kMemStream / kMemKeep
+    int32_t pt_vec;                     // page ids read as 16-byte vectors: B <= kSearchRequests, table
+                                        // 16-byte aligned, maxp a multiple of 4, paged, not redirected
     int32_t interleave;                 // items per round-robin span, 0 = one range per workgroup
     int32_t grid;                       // workgroups launched (set by the launcher)
 };

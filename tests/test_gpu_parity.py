@@ -804,6 +804,47 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(a, b), f"replay {rep} differs from eager"
 
 
+@pytest.mark.parametrize("maxp_pad", [0, 1])
+@pytest.mark.parametrize("where", ["first", "middle", "last", "before_first", "after_last"])
+def test_page_ids_read_as_vectors(where, maxp_pad):
+    """A few requests writing many pages each, with prior lengths that put
+    the first written column at every offset inside a 16-byte vector: with a
+    page-table row length that is a multiple of 4 the ids are read as
+    vectors, otherwise one by one.  A bad id in the first, a middle or the
+    last written column of a request rejects the call; a bad id in the
+    column just before the first written one or just after the last (read in
+    the same vector, not written) leaves it valid."""
+    q = np.array([37, 5, 0, 61, 19, 44], dtype=np.int64)
+    prior = np.array([3, 6, 9, 2, 0, 13], dtype=np.int64)
+    ps = 2
+    need = (q + prior + ps - 1) // ps
+    maxp = int(-(-int(need.max() + 2) // 4) * 4) + maxp_pad
+    assert (maxp % 4 == 0) == (maxp_pad == 0)
+    inp = W.nra_case(seed=881, q_lens=q, prior_lens=prior, Hq=8, Hkv=1, D=128, page_size=ps, maxp=maxp,
+                     kv_fp8=True, k_scale=0.05, v_scale=0.05, q_mode=W.Q_FP8_DYNAMIC)
+    b = 3
+    sl, ql = int(inp.seq_lens[b]), int(q[b])
+    lo, hi = (sl - ql) // ps, (sl - 1) // ps
+    assert lo % 4 == 1 and hi - lo > 8 and hi + 1 < maxp
+    col = {"first": lo, "middle": (lo + hi) // 2, "last": hi, "before_first": lo - 1, "after_last": hi + 1}[where]
+    inp.page_table[b, col] = inp.num_pages + 2
+    if where in ("before_first", "after_last"):
+        stats = run_and_compare(inp)
+        assert (H.oracle_outputs(inp)["flags"] == 0).all()
+        print(stats, flush=True)
+        return
+    dev = H.DeviceNra(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    gpu = dev.host_outputs()
+    assert (gpu["flags"] == -1).all()
+    H.check_exact(gpu["k_cache"], inp.k_cache0, "k_cache")
+    H.check_exact(gpu["v_cache"], inp.v_cache0, "v_cache")
+    H.check_exact(gpu["q_out"], inp.q_out0, "q_out")
+    assert (H.oracle_outputs(inp)["flags"] == -1).all()
+
+
 @pytest.mark.parametrize("seed", [1, 2, 3])
 def test_every_written_page_is_checked(seed):
     """Corrupt one randomly chosen page id among those the call writes (many
