@@ -83,6 +83,9 @@ struct MlaCursor {
     }
 };
 
+// read by the load slots past a wave's run; never written
+__device__ __align__(16) const uint16_t g_mla_zero[8] = {};
+
 template <bool KVFP8, bool NT>
 __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) {
     constexpr int U = kBatch;
@@ -121,11 +124,15 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     MlaCursor ld{0, 0, 0}, pr{0, 0, 0};
     uint4 bufA[U][2], bufB[U][2];
 
-    // two 16-byte loads per lane per chunk, always issued (clamped rows)
+    // two 16-byte loads per lane per chunk, always issued: rows past the
+    // run or heads past H read a 16-byte zero vector that stays in the
+    // caches, so that the last batch of a tile does not wait for a memory
+    // round trip of its own
     auto load_batch = [&](uint4 (&buf)[U][2]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int t = ld.left > 0 ? ld.t : t_first;
+            const bool live = ld.left > 0;
+            const int t = live ? ld.t : t_first;
             const uint16_t* p0;
             const uint16_t* p1;
             if (ld.c < n_qchunks) {
@@ -133,11 +140,11 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
                 // whole 128-byte rope slice (mirror_exchange completes them)
                 const int ha = ld.c * kHeadsPerWave + (grp & ~1), hb = ha + 1;
                 const uint16_t* q = a.q + (int64_t)t * a.q_token_stride + a.nope_dim;
-                p0 = q + (int64_t)(ha < a.H ? ha : 0) * a.q_head_stride + q_off0;
-                p1 = q + (int64_t)(hb < a.H ? hb : 0) * a.q_head_stride + q_off1;
+                p0 = live && ha < a.H ? q + (int64_t)ha * a.q_head_stride + q_off0 : g_mla_zero;
+                p1 = live && hb < a.H ? q + (int64_t)hb * a.q_head_stride + q_off1 : g_mla_zero;
             } else {
-                p0 = a.kv_c + (int64_t)t * a.kv_c_stride + 8 * lane;
-                p1 = a.k_pe + (int64_t)t * a.k_pe_stride + 8 * (lane & 7);
+                p0 = live ? a.kv_c + (int64_t)t * a.kv_c_stride + 8 * lane : g_mla_zero;
+                p1 = live ? a.k_pe + (int64_t)t * a.k_pe_stride + 8 * (lane & 7) : g_mla_zero;
             }
             buf[u][0] = ld16(p0);
             buf[u][1] = ld16(p1);
