@@ -83,6 +83,19 @@ struct MlaCursor {
     }
 };
 
+// element offset of cache slot `slot` (0 <= slot < capacity)
+__device__ __forceinline__ int64_t cache_row(const MlaDevArgs& a, int64_t slot, int row_len) {
+    int64_t blk, in;
+    if (a.capacity <= INT32_MAX) {
+        blk = fdiv31((int)slot, a.bs_div);
+        in = slot - blk * a.block_size;
+    } else {
+        blk = slot / a.block_size;
+        in = slot % a.block_size;
+    }
+    return blk * a.block_stride + in * (int64_t)row_len;
+}
+
 // read by the load slots past a wave's run; never written
 __device__ __align__(16) const uint16_t g_mla_zero[8] = {};
 
@@ -118,8 +131,9 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     float inv_scale = 1.0f;
     kv_t* cache = reinterpret_cast<kv_t*>(a.kv_cache);
 
-    const int blo = (int)((int64_t)a.total_items * blockIdx.x / a.grid);
-    const int bhi = (int)((int64_t)a.total_items * (blockIdx.x + 1) / a.grid);
+    // total * b / grid = items_q * b + items_r * b / grid (items_r * b < grid^2)
+    const int blo = a.items_q * (int)blockIdx.x + fdiv31(a.items_r * (int)blockIdx.x, a.grid_div);
+    const int bhi = a.items_q * ((int)blockIdx.x + 1) + fdiv31(a.items_r * ((int)blockIdx.x + 1), a.grid_div);
     int sub_lo = blo, sub_hi = blo, t_first = 0, ntok = 0;
     MlaCursor ld{0, 0, 0}, pr{0, 0, 0};
     uint4 bufA[U][2], bufB[U][2];
@@ -152,13 +166,13 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
         }
     };
     auto start_tile = [&]() {
-        t_first = sub_lo / CPT;
+        t_first = fdiv31(sub_lo, a.cpt_div);
         sub_hi = min(bhi, (t_first + TPB) * CPT);
-        ntok = (sub_hi - 1) / CPT - t_first + 1;
+        ntok = fdiv31(sub_hi - 1, a.cpt_div) - t_first + 1;
         const int n = sub_hi - sub_lo;
         const int w_lo = sub_lo + n * wave / 4;
         const int w_hi = sub_lo + n * (wave + 1) / 4;
-        ld.t = w_lo / CPT;
+        ld.t = fdiv31(w_lo, a.cpt_div);
         ld.c = w_lo - ld.t * CPT;
         ld.left = w_hi - w_lo;
         pr = ld;
@@ -182,9 +196,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
         const float4 cs = ldf4(a.cos_sin + (pc_ok ? pc : 0) * kRope + 4 * c4);
         if (tid < ntok) {
             s_pos[tid] = (pt >= 0 && pt < a.cs_rows) ? (int)pt : -1;
-            s_row[tid] = (slot >= 0 && slot < a.capacity)
-                             ? (slot / a.block_size) * a.block_stride + (slot % a.block_size) * (int64_t)row_len
-                             : -1;
+            s_row[tid] = (slot >= 0 && slot < a.capacity) ? cache_row(a, slot, row_len) : -1;
         }
         if (tid < ntok * (kRope / 4) && pc_ok) *reinterpret_cast<float4*>(s_cs + ic * kRope + 4 * c4) = cs;
     };
@@ -279,6 +291,14 @@ __global__ __launch_bounds__(kBlockThreads) void mla_kernel(const MlaDevArgs a) 
     }
 }
 
+void set_divisors(MlaDevArgs& la) {
+    la.grid_div = make_fastdiv31((uint32_t)la.grid);
+    la.cpt_div = make_fastdiv31((uint32_t)(la.chunks_per_token > 0 ? la.chunks_per_token : 1));
+    la.bs_div = make_fastdiv31((uint32_t)la.block_size);
+    la.items_q = (int)(la.total_items / la.grid);
+    la.items_r = (int)(la.total_items % la.grid);
+}
+
 template <bool KVFP8, bool NT>
 hipError_t launch_t(const MlaDevArgs& a, hipStream_t stream) {
     MlaDevArgs la = a;
@@ -287,6 +307,7 @@ hipError_t launch_t(const MlaDevArgs& a, hipStream_t stream) {
     int64_t want = (a.total_items + 7) / 8;
     if (want < 1) want = 1;
     la.grid = (int)(want < cap ? want : cap);
+    set_divisors(la);
     (void)hipGetLastError();   // the status below then covers this launch only
     hipLaunchKernelGGL((mla_kernel<KVFP8, NT>), dim3(la.grid), dim3(kBlockThreads), 0, stream, la);
     return hipGetLastError();
@@ -441,7 +462,7 @@ __global__ __launch_bounds__(kBlockThreads) void mla_q8_kernel(const MlaDevArgs 
             pe_hi.z = __shfl(pe.z, lane + 4, 64);
             pe_hi.w = __shfl(pe.w, lane + 4, 64);
             if (slot >= 0 && slot < a.capacity) {
-                kv_t* dst = cache + (slot / a.block_size) * a.block_stride + (slot % a.block_size) * (int64_t)row_len;
+                kv_t* dst = cache + cache_row(a, slot, row_len);
                 if constexpr (KVFP8) {
                     float x[8];
                     unpack8(kvv, x);
@@ -483,6 +504,7 @@ hipError_t launch_q8_t(const MlaDevArgs& a, hipStream_t stream) {
     int64_t cap = resident_grid(reinterpret_cast<const void*>(&mla_q8_kernel<QMODE, KVFP8, NT>), 0);
     if (cap < 1) cap = 256;
     la.grid = (int)(a.T < cap ? a.T : cap);
+    set_divisors(la);
     (void)hipGetLastError();   // the status below then covers this launch only
     hipLaunchKernelGGL((mla_q8_kernel<QMODE, KVFP8, NT>), dim3(la.grid), dim3(kBlockThreads), 0, stream, la);
     return hipGetLastError();

@@ -712,8 +712,10 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     auto next_range = [&]() -> bool {
         if (a.interleave == 0) {
             if (range_k++ > 0) return false;
-            blo = (int)((int64_t)a.total_items * blockIdx.x / a.grid);
-            bhi = (int)((int64_t)a.total_items * (blockIdx.x + 1) / a.grid);
+            // total * b / grid = items_q * b + items_r * b / grid (items_r * b < grid^2)
+            const int b = blockIdx.x;
+            blo = a.items_q * b + fdiv31(a.items_r * b, a.grid_div);
+            bhi = a.items_q * (b + 1) + fdiv31(a.items_r * (b + 1), a.grid_div);
             return blo < bhi;
         }
         const int64_t span = a.interleave;
@@ -772,13 +774,13 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     };
     // tile bounds and this wave's run inside it
     auto start_tile = [&]() {
-        t_first = sub_lo / CPT;
+        t_first = fdiv31(sub_lo, a.cpt_div);
         sub_hi = min(bhi, (t_first + TPB) * CPT);
-        ntok = (sub_hi - 1) / CPT - t_first + 1;
+        ntok = fdiv31(sub_hi - 1, a.cpt_div) - t_first + 1;
         const int n = sub_hi - sub_lo;
         const int w_lo = sub_lo + n * wave / 4;
         const int w_hi = sub_lo + n * (wave + 1) / 4;
-        ld.t = w_lo / CPT;
+        ld.t = fdiv31(w_lo, a.cpt_div);
         ld.c = w_lo - ld.t * CPT;
         ld.left = w_hi - w_lo;
         pr = ld;
@@ -822,7 +824,15 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
                     koff = voff = (int64_t)t * a.kv_out_stride;
                     srow = t;
                 } else if (m.slot >= 0 && m.slot < (int64_t)a.num_pages * a.page_size) {
-                    const int64_t page = m.slot / a.page_size, row = m.slot % a.page_size;
+                    // (slot < num_pages * page_size: 31 bits when the pool has fewer slots)
+                    int64_t page, row;
+                    if ((int64_t)a.num_pages * a.page_size <= INT32_MAX) {
+                        page = fdiv31((int)m.slot, a.ps_div);
+                        row = m.slot - page * a.page_size;
+                    } else {
+                        page = m.slot / a.page_size;
+                        row = m.slot % a.page_size;
+                    }
                     koff = page * a.k_page_stride + row * row_elems;
                     voff = page * a.v_page_stride + row * row_elems;
                     srow = m.slot;
@@ -906,12 +916,14 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     // requests, the tail of request blockIdx % B is instead split across all
     // workgroups with that index: one workgroup clearing a whole 64-row
     // page tail would start its token items late and end the kernel late.
-    const int r_lo = (int)((int64_t)a.B * blockIdx.x / a.grid);
-    const int r_hi = (int)((int64_t)a.B * (blockIdx.x + 1) / a.grid);
+    // (B * (grid + 1) < 2^31: B <= kMaxRequests)
+    const int r_lo = fdiv31(a.B * (int)blockIdx.x, a.grid_div);
+    const int r_hi = fdiv31(a.B * ((int)blockIdx.x + 1), a.grid_div);
     const bool tail_spread = a.paged && a.B <= a.grid;
-    const int t_req = tail_spread ? (int)(blockIdx.x % a.B) : 0;
-    const int t_slice = tail_spread ? (int)(blockIdx.x / a.B) : 0;
-    const int t_nslices = tail_spread ? (a.grid - 1 - t_req) / a.B + 1 : 1;
+    const int bq = fdiv31((int)blockIdx.x, a.b_div);
+    const int t_req = tail_spread ? (int)blockIdx.x - bq * a.B : 0;
+    const int t_slice = tail_spread ? bq : 0;
+    const int t_nslices = tail_spread ? fdiv31(a.grid - 1 - t_req, a.b_div) + 1 : 1;
     // page ids of the tails this workgroup clears (first kTailPrefetch requests)
     auto fetch_tail = [&]() {
         const int b = tail_spread ? t_req : min(r_lo + tid, max(r_hi - 1, 0));
@@ -1063,7 +1075,8 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
     // ------------------ requests: flags and tail clear ------------------
     // (issued before the token items so the zero stores drain while the
     // rows are processed)
-    // slice `slice` of `nslices` of the tail rows of request b (seq_len sl > 0)
+    // slice `slice` of `nslices` of the tail rows of request b (seq_len sl > 0):
+    // the 4 KiB pieces slice, slice + nslices, ... (whole lines, no division)
     auto clear_tail = [&](int sl, int64_t page, int slice, int nslices) {
         const int pcol = fdiv31(sl - 1, a.ps_div);
         const int last = (sl - 1) - pcol * a.page_size;
@@ -1073,8 +1086,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
         char* vb = reinterpret_cast<char*>(reinterpret_cast<kv_t*>(a.v_cache) + page * a.v_page_stride +
                                            (last + 1) * row_elems);
         const uint4 z = make_uint4(0, 0, 0, 0);
-        const int64_t v1 = nvec * (slice + 1) / nslices;
-        for (int64_t i = nvec * slice / nslices + tid; i < v1; i += kBlockThreads) {
+        for (int64_t i = (int64_t)slice * kBlockThreads + tid; i < nvec; i += (int64_t)kBlockThreads * nslices) {
             st16_stream(kb + 16 * i, z);
             st16_stream(vb + 16 * i, z);
         }
@@ -1083,8 +1095,7 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
             const int64_t ns = (int64_t)a.Hkv * kc.kv_ng;
             const int64_t first = (page * a.page_size + last + 1) * ns;
             const int64_t cnt = (int64_t)(a.page_size - 1 - last) * ns;
-            const int64_t c1 = cnt * (slice + 1) / nslices;
-            for (int64_t i = cnt * slice / nslices + tid; i < c1; i += kBlockThreads) {
+            for (int64_t i = (int64_t)slice * kBlockThreads + tid; i < cnt; i += (int64_t)kBlockThreads * nslices) {
                 a.k_scale_out[first + i] = 0.0f;
                 a.v_scale_out[first + i] = 0.0f;
             }
@@ -1195,6 +1206,11 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     // in that mode and is not done.  Short calls keep one contiguous range
     // each.
     la.interleave = (a.T >= 8 * (int64_t)la.grid) ? 24 : 0;
+    la.grid_div = make_fastdiv31((uint32_t)la.grid);
+    la.cpt_div = make_fastdiv31((uint32_t)(a.chunks_per_token > 0 ? a.chunks_per_token : 1));
+    la.b_div = make_fastdiv31((uint32_t)(a.B > 0 ? a.B : 1));
+    la.items_q = (int)(a.total_items / la.grid);
+    la.items_r = (int)(a.total_items % la.grid);
     (void)hipGetLastError();   // the status below then covers this launch only
     hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, ROT, MEM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();

@@ -106,6 +106,11 @@ struct NraDevArgs {
                                         // 16-byte aligned, maxp a multiple of 4, paged, not redirected
     int32_t interleave;                 // items per round-robin span, 0 = one range per workgroup
     int32_t grid;                       // workgroups launched (set by the launcher)
+    // divisions of the launch geometry without a division instruction (set
+    // by the launcher): by grid, by chunks_per_token, by B (1 when B = 0),
+    // and total_items = items_q * grid + items_r
+    FastDiv31 grid_div, cpt_div, b_div;
+    int32_t items_q, items_r;
 };
 
 struct MlaDevArgs {
@@ -139,6 +144,11 @@ struct MlaDevArgs {
     int32_t chunks_per_token;           // ceil(H / heads per wave) + 1 latent chunk
     int64_t total_items;
     int32_t grid;                       // workgroups launched (set by the launcher)
+    // divisions without a division instruction (set by the launcher): by
+    // grid, by chunks_per_token, by block_size (used when capacity < 2^31),
+    // and total_items = items_q * grid + items_r
+    FastDiv31 grid_div, cpt_div, bs_div;
+    int32_t items_q, items_r;
 };
 
 // Workgroups of kBlockThreads threads that `kernel` keeps resident on the
