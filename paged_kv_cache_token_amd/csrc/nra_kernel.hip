@@ -1183,11 +1183,18 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     // 8-item split measured best.  A decode with few head rows per token and
     // long tails (8/1 heads, page 64, 256 requests) otherwise gives each
     // workgroup four requests' tails: one per request took it from 14.8 to
-    // 12.6 us.
+    // 12.6 us.  With fewer requests than CUs, each request's tail is split
+    // over B * floor(256 / B) workgroups (about one per CU of the 256), so
+    // that the zero stores of a few long page tails leave from every CU
+    // instead of a handful: the 1-request decode with a 63-row page-64 tail
+    // 7.0 -> 6.6 us, 32 requests with 64/8 heads 8.2 -> 7.3, the 16-token
+    // decode 6.3 -> 6.0; neutral from 128 requests up.
     int64_t want = (a.total_items + 7) / 8;
     const int64_t want4 = (a.total_items + 3) / 4;
     if (want < (want4 < 64 ? want4 : 64)) want = want4 < 64 ? want4 : 64;
-    const int64_t per_req = a.zero_tail ? a.B : (a.B + 3) / 4;
+    const int64_t per_req = !a.zero_tail ? (a.B + 3) / 4
+                            : (a.B > 0 && a.B < kTailSpreadGroups) ? (int64_t)a.B * (kTailSpreadGroups / a.B)
+                                                                   : a.B;
     if (want < per_req) want = per_req;
     if (want < 1) want = 1;
     NraDevArgs la = a;

@@ -19,6 +19,9 @@ constexpr int kMaxStagedQHeads = 256;
 constexpr int kBatch = 2;
 // tail pages of the first requests a workgroup clears, prefetched with the metadata
 constexpr int kTailPrefetch = 16;
+// workgroups that share the tail clears of a call with fewer requests
+// (one per CU of the 256 CUs of the part)
+constexpr int kTailSpreadGroups = 256;
 // up to this many requests the validation finds a page's request by binary
 // search, and reads the page ids as 16-byte vectors when the table allows it
 constexpr int kSearchRequests = 64;
