@@ -791,7 +791,9 @@ def stream_calibration(args, dev):
     343.9 MB, writes 172.4 MB) in the roofline protocol (rotating sets, 20
     warm-ups, sessions of back-to-back launches with one event pair): an
     elementwise bf16 add c = a + b (2 reads : 1 write, the prefill's mix), a
-    copy (1 : 1) and a sum (read only).  torch's kernels use ordinary loads
+    copy (1 : 1) and a sum (read only); and the MLA call's strided pattern
+    (an in-place scale of the 128-byte rope slice of every 384-byte query
+    head) beside an in-place scale of a contiguous tensor of the same bytes.  torch's kernels use ordinary loads
     and stores.  A reference for what the memory system gives a simple
     kernel in this protocol, not a bound."""
     import torch
@@ -819,6 +821,28 @@ def stream_calibration(args, dev):
         a, b, _ = nxt()
         torch.sum(a)
     arms = {"add_2r1w": (add, 2 * n * 2 + n * 2), "copy_1r1w": (copy, 2 * n * 2), "sum_read": (rsum, n * 2)}
+
+    # The MLA call's in-place RoPE touches 128 bytes of every 384-byte query
+    # head (the rope slice of [T=4096, H=128, 128 nope + 64 rope] bf16): an
+    # in-place scale of exactly that strided view, and of a contiguous tensor
+    # of the same size, give what a library elementwise kernel gets from
+    # this read-modify-write pattern in the same protocol.
+    T, H, DN, DR = 4096, 128, 128, 64
+    qsets = [torch.randn(T, H, DN + DR, device=dev, dtype=torch.bfloat16)
+             for _ in range(max(4, -(-SET_TARGET_BYTES // (T * H * (DN + DR) * 2))))]
+    csets = [torch.randn(T * H * DR, device=dev, dtype=torch.bfloat16) for _ in range(len(qsets))]
+    kq = {"i": 0}
+
+    def rope_slice_rmw():
+        kq["i"] = (kq["i"] + 1) % len(qsets)
+        qsets[kq["i"]][:, :, DN:].mul_(1.0)
+
+    def contig_rmw():
+        kq["i"] = (kq["i"] + 1) % len(csets)
+        csets[kq["i"]].mul_(1.0)
+    slice_bytes = 2 * T * H * DR * 2
+    arms["mla_rope_slice_rmw"] = (rope_slice_rmw, slice_bytes)
+    arms["contiguous_rmw_same_bytes"] = (contig_rmw, slice_bytes)
     out = {}
     for name, (fn, nbytes) in arms.items():
         for _ in range(20):
@@ -834,7 +858,8 @@ def stream_calibration(args, dev):
                      "GBps": round(nbytes / (med * 1e-6) / 1e9, 1),
                      "pct_of_peak": round(100 * nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
         log(f"{name}: {out[name]}")
-    print(json.dumps({"stream_calibration": out, "sets": S, "note": "torch kernels, ordinary loads/stores"}),
+    print(json.dumps({"stream_calibration": out, "sets": S, "mla_sets": len(qsets),
+                      "note": "torch kernels, ordinary loads/stores"}),
           flush=True)
 
 
