@@ -84,10 +84,12 @@ typedef enum { QKPREP_ADDR_PAGED = 0, QKPREP_ADDR_SLOT = 1 } qkprep_addressing;
  * latent rows and the E4M3 MLA query).  Not on the pages, which leave the
  * store path open; a choice of this library, measured on MI355X. */
 typedef enum {
-    QKPREP_STORE_STREAM = 0,   /* default: non-temporal stores, so that the written rows drain
+    QKPREP_STORE_STREAM = 0,   /* default: non-temporal stores for the long contiguous rows (Q
+                                  rows, the MLA latent rows and rope slices), so that they drain
                                   to HBM as they are produced instead of occupying L2 and the
-                                  Infinity Cache; rows written back into qkv (in-place Q / K)
-                                  keep ordinary stores */
+                                  Infinity Cache; K/V cache rows of the norm-rope-append call
+                                  and rows written back into qkv (in-place Q / K) keep ordinary
+                                  stores (measured faster for those) */
     QKPREP_STORE_KEEP = 1      /* ordinary stores everywhere: the rows stay in L2 / the
                                   Infinity Cache for a kernel that reads them right after */
 } qkprep_store_policy;

@@ -48,7 +48,8 @@ inline FastDiv31 make_fastdiv31(uint32_t d) {
 
 // Memory modes of the norm-rope-append kernel: Q or K written back into
 // qkv (cached loads and stores); qkv read once with streaming loads, and the
-// token rows stored with streaming (non-temporal) or ordinary stores.
+// Q rows stored with streaming (non-temporal) or ordinary stores (K/V cache
+// rows always take ordinary stores).
 enum : int { kMemInPlace = 0, kMemStream = 1, kMemKeep = 2 };
 
 struct NraDevArgs {
