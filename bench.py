@@ -23,7 +23,9 @@ launches' dirty output lines are written back to HBM while it runs: the
 steady state of a serving loop.  The timed steps rotate the same way.
 
 Per-kernel timing (the roofline): 20 warm-up launches of each kernel, then
-3 sessions; in each, every kernel gets 20 more untimed launches and then a
+3 sessions; in each, every kernel gets at least 20 more untimed launches
+(and about 60 ms of its own work: a bandwidth-bound kernel that follows a
+light one, the decode, runs 1-2 % slower for some tens of milliseconds) and then a
 timed back-to-back run of 200 rotating launches with one HIP event pair on
 the launch stream (no marker between launches: on this GPU an event marker
 delays the next kernel by several microseconds); the kernel order
@@ -58,6 +60,8 @@ HBM_PEAK_GBS = 8000.0
 # rotating sets: at least 4, and more than 1 GiB of touched memory in all
 SET_TARGET_BYTES = int(1.1 * (1 << 30))
 MIN_SETS, MAX_SETS = 4, 128
+# untimed work of an arm right before each of its timed sessions
+ARM_WARMUP_MS = 60.0
 
 
 def log(msg):
@@ -70,6 +74,8 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sessions", type=int, default=3)
+    ap.add_argument("--arm-warmup-ms", type=float, default=ARM_WARMUP_MS,
+                    help="untimed work of an arm right before each of its timed sessions (at least 20 launches)")
     ap.add_argument("--session-launches", type=int, default=200,
                     help="rotating launches of each kernel per session")
     ap.add_argument("--flush-launches", type=int, default=50,
@@ -507,7 +513,8 @@ class Flushes:
 def measure_arms(rots, args, stream, flushes):
     """The roofline protocol over several kernels ("arms"): 20 warm-up
     launches each, then args.sessions sessions of args.session_launches
-    rotating launches per arm, the arm order alternating between sessions;
+    rotating launches per arm, each after max(20, ~ARM_WARMUP_MS of work)
+    untimed launches of the same arm, the arm order alternating between sessions;
     then the extra modes (back-to-back on one set, single launches after a
     read or a write flush)."""
     import torch
@@ -516,6 +523,12 @@ def measure_arms(rots, args, stream, flushes):
         for _ in range(20):
             rots[n].launch("warmup")
     torch.cuda.synchronize()
+    # per-session warm-up of each arm: at least 20 launches and about
+    # ARM_WARMUP_MS of the arm's own work (from a short timed estimate)
+    warm = {}
+    for n in names:
+        est = time_run(lambda: rots[n].launch("warmup"), 20, stream)
+        warm[n] = max(20, int(math.ceil(args.arm_warmup_ms * 1e3 / max(est, 1e-3))))
     sess = {n: [] for n in names}
     orders = []
     for s in range(args.sessions):
@@ -523,10 +536,10 @@ def measure_arms(rots, args, stream, flushes):
         orders.append(list(order))
         for n in order:
             r = rots[n]
-            # 20 more untimed launches right before each timed run: a kernel
-            # that follows a light one (the decode) otherwise runs its first
+            # untimed launches right before each timed run: a kernel that
+            # follows a light one (the decode) otherwise runs its first
             # milliseconds on a memory system not yet at full speed
-            for _ in range(20):
+            for _ in range(warm[n]):
                 r.launch(f"warmup_s{s + 1}")
             sess[n].append(time_run(lambda: r.launch(f"rotating_s{s + 1}"), args.session_launches, stream))
     res = {}
