@@ -725,7 +725,19 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
             return blo < bhi;
         }
         const int64_t span = a.interleave;
-        const int64_t tile = blockIdx.x + (int64_t)(range_k++) * a.grid;
+        // Workgroup b takes span sidx(b) of every round, a permutation of
+        // [0, grid) under which runs of kXcdRun consecutive spans land on one
+        // XCD (the dispatcher deals workgroups to the kXcds XCDs round-robin
+        // by index): the padded Q-scale pieces
+        // of neighbouring spans then meet in one L2 and leave it as whole
+        // lines, while the round still covers the same narrow window of qkv.
+        // (Identity when the grid is not a multiple of kXcds * kXcdRun.)
+        int64_t sidx = blockIdx.x;
+        if (a.grid % (kXcds * kXcdRun) == 0) {
+            const int b = blockIdx.x, xcd = b % kXcds, slot = b / kXcds;
+            sidx = (int64_t)(slot / kXcdRun) * (kXcds * kXcdRun) + xcd * kXcdRun + slot % kXcdRun;
+        }
+        const int64_t tile = sidx + (int64_t)(range_k++) * a.grid;
         if (tile * span >= a.total_items) return false;
         blo = (int)(tile * span);
         bhi = (int)min((int64_t)a.total_items, tile * span + span);
@@ -1214,9 +1226,11 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     // 88.5 us against 4-token spans (40 items), the 16k one 103.6 -> 95.8,
     // 64-dim heads 52.5 -> 51.4, the strided 256-dim one 50.8 -> 49.3; 20 to
     // 32 items are close, 12 or 16 items slower (the per-tile metadata round
-    // then dominates), 48 slower.  Grouping a round's spans by XCD (so that
-    // one L2 merges the padded Q scales into whole lines) measured 5 us slower
-    // in that mode and is not done.  Short calls keep one contiguous range
+    // then dominates), 48 slower.  Spans are dealt to the XCDs in runs of
+    // kXcdRun (see next_range): runs of 16 or 32 spans took the 16k-token
+    // prefill from 90.9 to 87.4 us and the T = 14 876 draw from 83.5 to
+    // 81.2 us, while runs of 64 or 128 (each XCD a contiguous eighth of the
+    // round) were slower than none.  Short calls keep one contiguous range
     // each.
     la.interleave = (a.T >= 8 * (int64_t)la.grid) ? 24 : 0;
     la.grid_div = make_fastdiv31((uint32_t)la.grid);

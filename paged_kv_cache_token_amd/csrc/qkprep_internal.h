@@ -19,6 +19,10 @@ constexpr int kMaxStagedQHeads = 256;
 constexpr int kBatch = 2;
 // tail pages of the first requests a workgroup clears, prefetched with the metadata
 constexpr int kTailPrefetch = 16;
+// XCDs of the part (workgroups are dealt to them round-robin by index) and
+// the number of consecutive round-robin spans of a long call kept on one XCD
+constexpr int kXcds = 8;
+constexpr int kXcdRun = 16;
 // workgroups that share the tail clears of a call with fewer requests
 // (one per CU of the 256 CUs of the part)
 constexpr int kTailSpreadGroups = 256;
