@@ -614,7 +614,7 @@ struct Cursor {
     }
 };
 
-template <int D, int QMODE, bool KVFP8, int ROT, int MEM>
+template <int D, int QMODE, bool KVFP8, int ROT, int MEM, bool TL>
 __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4))) void nra_kernel(const NraDevArgs a) {
     constexpr bool PART = ROT == kRotPart;
     constexpr bool NTL = MEM != kMemInPlace;     // qkv read once: streaming loads
@@ -1119,22 +1119,29 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
             }
         }
     };
-    for (int b = r_lo; a.paged && b < r_hi; ++b) {
-        for (int h = tid; h < a.Hkv; h += kBlockThreads) a.flags[(int64_t)b * a.Hkv + h] = bad ? -1 : 0;
-        if (bad || !a.zero_tail || tail_spread) continue;
-        const int sl = s_seqlen[b];
-        if (sl <= 0) continue;
-        // (an LDS read for the prefetched pages; a select between the two
-        // would become a flat load whose wait drains every store in flight)
-        int64_t page;
-        if (b - r_lo < kTailPrefetch)
-            page = s_tail[b - r_lo];
-        else
-            page = gld(a.page_table + (int64_t)b * a.maxp + fdiv31(sl - 1, a.ps_div));
-        clear_tail(sl, page, 0, 1);
-    }
-    if (tail_spread && !bad && a.zero_tail && s_seqlen[t_req] > 0)
+    // Flags of this workgroup's requests, then the tail clears: before the
+    // token rows (their zero stores drain while the rows are processed) or,
+    // in the TL instances, after them (one copy in each instance).
+#define QKPREP_NRA_FLAGS_AND_TAILS()                                                                      \
+    for (int b = r_lo; a.paged && b < r_hi; ++b) {                                                        \
+        for (int h = tid; h < a.Hkv; h += kBlockThreads) a.flags[(int64_t)b * a.Hkv + h] = bad ? -1 : 0;  \
+        if (bad || !a.zero_tail || tail_spread) continue;                                                 \
+        const int sl = s_seqlen[b];                                                                       \
+        if (sl <= 0) continue;                                                                            \
+        /* (an LDS read for the prefetched pages; a select between the two                                \
+        would become a flat load whose wait drains every store in flight) */                              \
+        int64_t page;                                                                                     \
+        if (b - r_lo < kTailPrefetch)                                                                     \
+            page = s_tail[b - r_lo];                                                                      \
+        else                                                                                              \
+            page = gld(a.page_table + (int64_t)b * a.maxp + fdiv31(sl - 1, a.ps_div));                    \
+        clear_tail(sl, page, 0, 1);                                                                       \
+    }                                                                                                     \
+    if (tail_spread && !bad && a.zero_tail && s_seqlen[t_req] > 0)                                        \
         clear_tail(s_seqlen[t_req], s_tail[0], t_slice, t_nslices);
+    if constexpr (!TL) {
+        QKPREP_NRA_FLAGS_AND_TAILS();
+    }
 
     // ---------------------------- token items ----------------------------
     if (have_items && !bad) {
@@ -1182,8 +1189,10 @@ __global__ __launch_bounds__(kBlockThreads) __attribute__((amdgpu_waves_per_eu(4
             __syncthreads();
         }
     }
-
-
+    if constexpr (TL) {
+        QKPREP_NRA_FLAGS_AND_TAILS();
+    }
+#undef QKPREP_NRA_FLAGS_AND_TAILS
 }
 
 template <int D, int QMODE, bool KVFP8, int ROT, int MEM>
@@ -1193,7 +1202,7 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     // enough workgroups to fill every CU, none with less than 8 head-row
     // chunks of work, and at least one per request when tails are cleared
     // (one per 4 requests otherwise, for the flags)
-    int64_t cap = resident_grid(reinterpret_cast<const void*>(&nra_kernel<D, QMODE, KVFP8, ROT, MEM>), lds);
+    int64_t cap = resident_grid(reinterpret_cast<const void*>(&nra_kernel<D, QMODE, KVFP8, ROT, MEM, false>), lds);
     if (cap < 1) cap = 256;
     // 8 (token, chunk) items per workgroup, but 4 for small calls (up to 64
     // workgroups): a tiny decode's time is its latency chain, which more
@@ -1239,7 +1248,20 @@ hipError_t launch_t(const NraDevArgs& a, hipStream_t stream) {
     la.items_q = (int)(a.total_items / la.grid);
     la.items_r = (int)(a.total_items % la.grid);
     (void)hipGetLastError();   // the status below then covers this launch only
-    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, ROT, MEM>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
+    // Decodes of many requests with several head-row chunks per token clear
+    // the tails after the token rows (TL instances, whole-head rotary and
+    // streaming Q stores only): there the tails' stores otherwise delay the
+    // rows.  B = 256 decodes: 32/8 heads page 16 7.9 -> 7.6 us, 64/8 heads
+    // page 64 15.0 -> 13.4 us; smaller calls lose from it (their time is the
+    // latency chain plus one tail drain), 8/1 heads (two chunks) gain nothing.
+    if constexpr (ROT == kRotWhole && MEM == kMemStream) {
+        if (la.interleave == 0 && a.zero_tail && a.B >= kTailsLastRequests && a.chunks_per_token >= 4) {
+            hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, ROT, MEM, true>), dim3(la.grid), dim3(kBlockThreads), lds,
+                               stream, la);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((nra_kernel<D, QMODE, KVFP8, ROT, MEM, false>), dim3(la.grid), dim3(kBlockThreads), lds, stream, la);
     return hipGetLastError();
 }
 

@@ -23,6 +23,8 @@ constexpr int kTailPrefetch = 16;
 // the number of consecutive round-robin spans of a long call kept on one XCD
 constexpr int kXcds = 8;
 constexpr int kXcdRun = 16;
+// decodes with at least this many requests clear the tails after the token rows
+constexpr int kTailsLastRequests = 256;
 // workgroups that share the tail clears of a call with fewer requests
 // (one per CU of the 256 CUs of the part)
 constexpr int kTailSpreadGroups = 256;

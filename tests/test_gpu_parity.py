@@ -598,6 +598,34 @@ def test_out_of_pool_page_short_validation_path(b, which, long_req):
     assert (H.oracle_outputs(inp)["flags"] == -1).all()
 
 
+@pytest.mark.parametrize("q_mode,kv_fp8", [(W.Q_BF16, False), (W.Q_FP8_DYNAMIC, True), (W.Q_FP8_STATIC, True)])
+@pytest.mark.parametrize("bad", [None, 0, 255])
+def test_decodes_that_clear_tails_after_the_rows(q_mode, kv_fp8, bad):
+    """Decodes of 256 or more requests with at least 4 head-row chunks per
+    token (32/8/128 heads: 6) clear the page tails after the token rows.
+    Valid calls match the oracle (tails zeroed, rows, flags); a page id past
+    the pool in request 0 or 255 rejects the whole call and writes nothing."""
+    B = 256
+    rng = np.random.default_rng(720)
+    prior = rng.integers(0, 60, B)
+    inp = W.nra_case(seed=721, q_lens=np.ones(B, dtype=np.int64), prior_lens=prior, Hq=32, Hkv=8, D=128,
+                     page_size=16, maxp=8, q_mode=q_mode, kv_fp8=kv_fp8, k_scale=0.05 if kv_fp8 else 1.0,
+                     v_scale=0.05 if kv_fp8 else 1.0, q_scale_inv=4.0 if q_mode == W.Q_FP8_STATIC else 1.0)
+    if bad is None:
+        run_and_compare(inp)
+        return
+    inp.page_table[bad, int(prior[bad]) // 16] = inp.num_pages + 3
+    dev = H.DeviceNra(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    gpu = dev.host_outputs()
+    assert (gpu["flags"] == -1).all()
+    H.check_exact(gpu["k_cache"], inp.k_cache0, "k_cache")
+    H.check_exact(gpu["v_cache"], inp.v_cache0, "v_cache")
+    assert (H.oracle_outputs(inp)["flags"] == -1).all()
+
+
 @pytest.mark.parametrize("long_req", [None, 0, 255])
 def test_short_and_full_validation_paths_agree_on_valid_calls(long_req):
     """The same 256 two-page requests, valid, with and without one request
