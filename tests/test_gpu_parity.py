@@ -217,6 +217,22 @@ def test_c5_mla_full_size():
     print(stats, flush=True)
 
 
+@pytest.mark.parametrize("q_mode", [W.Q_BF16, W.Q_FP8_DYNAMIC])
+def test_mla_long_call_at_the_grid_limits(q_mode):
+    """140 000 tokens of one head: the bf16-query launch wants 35 000
+    workgroups of 8 items and is capped at 32 768 (so each takes 8 or 9
+    items and the range split works near its 31-bit bound); the E4M3-query
+    launch loops each workgroup over about 45 tokens.  Every output against
+    the oracle."""
+    inp = W.mla_case(seed=730, T=140_000, H=1, num_blocks=2200, block_size=64, q_mode=q_mode, negative_slots=3)
+    dev = H.DeviceMla(inp)
+    dev.run()
+    torch.cuda.synchronize()
+    assert dev.guards_intact()
+    stats = H.compare_mla(inp, dev.host_outputs(), H.oracle_mla(inp))
+    H.assert_exact_floors(stats)
+
+
 # ----------------------------------------------------------------------------
 # variants on small shapes (several tiles and a ragged tail)
 # ----------------------------------------------------------------------------
